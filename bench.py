@@ -1,0 +1,162 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA chunked-prefill forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--no-cpu]
+
+A step is one kda_chunk_prefill_fwd call covering every head of one layer of
+the workload (default: 8 sequences x 2048 tokens, 16 heads, head_dim 128, fp32
+initial/final state; the 8x2048 shape of vLLM PR #55737's report, "Features
+and motivation").  Inputs are seeded synthetic data already resident in HBM.
+Two complete buffer sets are rotated so that consecutive steps do not find the
+previous step's data in the 256 MB last-level cache.
+
+Prints one JSON line: tokens/s (whole job), microseconds per layer, the HBM
+roofline of the dominant kernel (algorithmic bytes / measured launch time
+against 8 TB/s), and the fp64 oracle timed on the host cores as a reported
+baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s + µs/layer (8x2048, H=16, D=128); % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, AMD spec
+MFMA_BF16_PEAK_TF = 2500.0  # dense bf16, AMD spec
+
+
+def algorithmic_bytes(T, H, N, state_bytes, has_initial):
+    """Bytes the method must move: q, k, v, g (bf16) + beta logit (bf16) + out
+    (bf16) per (token, head); the state written once, read once if given."""
+    per_token_head = 4 * 128 * 2 + 2 + 128 * 2
+    per_seq_head = 128 * 128 * state_bytes * (2 if has_initial else 1)
+    return T * H * per_token_head + N * H * per_seq_head
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--sets", type=int, default=2, help="buffer sets rotated across steps")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the KDA forward has no cross-GPU path here", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kda_inputs as KI
+    import gated_delta_rule_tok_amd as kda
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = KI.config_inputs(args.config)
+    T, H, N = x.T, x.H, x.N
+    sbytes = 2 if x.state_bf16 else 4
+    sdtype = torch.bfloat16 if x.state_bf16 else torch.float32
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    base = dict(q=bf(x.q), k=bf(x.k), v=bf(x.v), g=bf(x.g), beta=bf(x.beta_logits),
+                A_log=torch.from_numpy(x.A_log).to(dev),
+                dt_bias=torch.from_numpy(x.dt_bias).to(dev),
+                cu=torch.from_numpy(x.cu_seqlens).to(dev))
+    if x.initial_state is None:
+        base["s0"] = None
+    elif x.state_bf16:
+        base["s0"] = bf(x.initial_state)
+    else:
+        base["s0"] = torch.from_numpy(x.initial_state).to(dev)
+    sets = []
+    for i in range(max(1, args.sets)):
+        s = base if i == 0 else {k: (None if v is None else v.clone()) for k, v in base.items()}
+        s["out"] = torch.empty(T, H, 128, dtype=torch.bfloat16, device=dev)
+        s["fin"] = torch.empty(N, H, 128, 128, dtype=sdtype, device=dev)
+        s["ws"] = torch.empty(max(1, kda.kda_get_workspace_size(T, H, N)), dtype=torch.uint8,
+                              device=dev)
+        sets.append(s)
+
+    def step(i):
+        s = sets[i % len(sets)]
+        kda.kda_chunk_prefill_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["A_log"],
+                                  s["dt_bias"], x.lower_bound, x.scale, s["s0"], s["cu"],
+                                  s["out"], s["fin"], s["ws"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+
+    ms_per_step = wall * 1e3 / args.steps
+    launch_ms = float(per_launch_ms.mean())
+    tokens_per_s = T / (ms_per_step * 1e-3)
+    abytes = algorithmic_bytes(T, H, N, sbytes, x.initial_state is not None)
+    achieved_gbs = abytes / (launch_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "us_per_layer": ms_per_step * 1e3,
+        "us_per_layer_event_median": float(np.median(per_launch_ms)) * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": x.meta["config"], "tokens": T, "sequences": N, "heads": H,
+                   "head_dim": 128, "state": "bf16" if x.state_bf16 else "fp32",
+                   "initial_state": x.initial_state is not None, "buffer_sets": len(sets)},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": abytes, "launch_us": launch_ms * 1e3},
+    }
+
+    if not args.no_cpu:
+        import oracle
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        c0 = time.perf_counter()
+        oracle.kda_oracle_fwd(x.q, x.k, x.v, x.g, x.beta_logits, x.A_log, x.dt_bias,
+                              x.lower_bound, x.scale, x.initial_state, x.cu_seqlens,
+                              threads=threads)
+        cpu_s = time.perf_counter() - c0
+        result["cpu_baseline"] = {
+            "value": T / cpu_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole {x.meta['config']} workload ({T} tokens x {H} heads), "
+                      f"fp64 token recurrence, {threads} threads over (sequence, head), "
+                      f"{cpu_s:.2f} s"}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

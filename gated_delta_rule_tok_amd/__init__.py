@@ -1,0 +1,177 @@
+"""Python binding of libkda.so, the MI355X (gfx950) KDA chunked-prefill forward.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/kda.h.  Tensors are torch tensors
+used as device memory; the stream defaults to torch's current stream.  There
+is no CPU fallback: if libkda.so is missing, every call raises.
+
+    ws = torch.empty(kda_get_workspace_size(T, H, N), dtype=torch.uint8, device="cuda")
+    kda_chunk_prefill_fwd(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, scale,
+                          initial_state, cu_seqlens, out, final_state, ws)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["kda_get_workspace_size", "kda_chunk_prefill_fwd", "kda_status_string",
+           "kda_last_hip_error", "kda_debug_set_vsplit", "KdaError", "library_path", "load_library"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+HEAD_DIM = 128
+KDA_OK = 0
+KDA_STATE_FP32 = 0
+KDA_STATE_BF16 = 1
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libkda.so once; raises if it has not been built.
+
+    torch's wheel carries its own HIP runtime (libamdhip64, SONAME
+    libamdhip64.so.7, the same SONAME as the system ROCm copy).  torch is
+    imported first so that its runtime is in the process before libkda.so is
+    mapped: the dynamic loader then resolves libkda.so's libamdhip64.so.7 to
+    that same copy.  Loading libkda.so first would bring in the system copy, and
+    torch would then load a second HIP runtime that sees no device.
+    """
+    global _lib
+    if _lib is None:
+        try:
+            import torch  # noqa: F401  (see above: one HIP runtime per process)
+        except ImportError:
+            pass
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with "
+                "`python -m gated_delta_rule_tok_amd.build` (there is no fallback path)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I32, I64, SZ, F = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                              ctypes.c_float)
+        lib.kda_get_workspace_size.argtypes = [I64, I32, I32]
+        lib.kda_get_workspace_size.restype = SZ
+        lib.kda_chunk_prefill_fwd.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P, P, P, P,
+                                              I64, I32, I32, ctypes.c_int, SZ]
+        lib.kda_chunk_prefill_fwd.restype = ctypes.c_int
+        lib.kda_status_string.argtypes = [ctypes.c_int]
+        lib.kda_status_string.restype = ctypes.c_char_p
+        lib.kda_last_hip_error.argtypes = []
+        lib.kda_last_hip_error.restype = ctypes.c_char_p
+        lib.kda_debug_set_vsplit.argtypes = [ctypes.c_int]
+        lib.kda_debug_set_vsplit.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def kda_get_workspace_size(max_tokens: int, heads: int, max_seqs: int) -> int:
+    return int(load_library().kda_get_workspace_size(int(max_tokens), int(heads), int(max_seqs)))
+
+
+def kda_status_string(status: int) -> str:
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def kda_last_hip_error() -> str:
+    return load_library().kda_last_hip_error().decode()
+
+
+def kda_debug_set_vsplit(s: int) -> int:
+    """Test hook: force the value split (1, 2, 4, 8) or 0 for automatic."""
+    prev = load_library().kda_debug_set_vsplit(int(s))
+    if prev < 0:
+        raise ValueError(f"invalid value split {s}")
+    return prev
+
+
+def _check(t, name, dtype, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (dense row-major)")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def kda_chunk_prefill_fwd(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound: float,
+                          scale: float, initial_state, cu_seqlens, out, final_state, workspace,
+                          stream=None) -> None:
+    """Queue one KDA chunked-prefill forward (see include/kda.h for the contract).
+
+    q, k, v, g, out [T, H, 128] bf16; beta_logits [T, H] bf16; A_log [H] fp32;
+    dt_bias [H, 128] fp32; initial_state None or [N, H, 128, 128]; final_state
+    [N, H, 128, 128] (fp32 or bf16, the same dtype as initial_state);
+    cu_seqlens [N + 1] int32; workspace uint8 (or None if no workspace is
+    needed); stream: a torch.cuda.Stream, a raw hipStream_t int, or None for
+    torch's current stream.  Leading singleton batch dims ([1, T, H, 128]) are
+    accepted.
+    """
+    import torch
+    lib = load_library()
+
+    def squeeze_batch(t):
+        return t[0] if (t is not None and t.dim() == 4 and t.shape[0] == 1
+                        and t.shape[-1] == HEAD_DIM and t.shape[-2] != HEAD_DIM) else t
+
+    q, k, v, g, out = (squeeze_batch(t) for t in (q, k, v, g, out))
+    if q.dim() != 3:
+        raise ValueError(f"q must be [T, H, {HEAD_DIM}], got {tuple(q.shape)}")
+    T, H, D = q.shape
+    if D != HEAD_DIM:
+        raise ValueError(f"head_dim must be {HEAD_DIM}, got {D}")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be [N + 1] with N >= 1")
+    N = cu_seqlens.numel() - 1
+    bf = torch.bfloat16
+    if final_state.dtype == torch.float32:
+        sdt = KDA_STATE_FP32
+    elif final_state.dtype == torch.bfloat16:
+        sdt = KDA_STATE_BF16
+    else:
+        raise TypeError(f"state dtype must be float32 or bfloat16, got {final_state.dtype}")
+    sshape = (N, H, HEAD_DIM, HEAD_DIM)
+    ptrs = [
+        _check(q, "q", bf, (T, H, D)), _check(k, "k", bf, (T, H, D)),
+        _check(v, "v", bf, (T, H, D)), _check(g, "g", bf, (T, H, D)),
+        _check(beta_logits.reshape(T, H) if beta_logits.numel() == T * H else beta_logits,
+               "beta_logits", bf, (T, H)),
+        _check(A_log.reshape(-1), "A_log", torch.float32, (H,)),
+        _check(dt_bias.reshape(H, -1), "dt_bias", torch.float32, (H, D)),
+    ]
+    s0 = None if initial_state is None else _check(initial_state, "initial_state",
+                                                   final_state.dtype, sshape)
+    cu = _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    o = _check(out, "out", bf, (T, H, D))
+    fs = _check(final_state, "final_state", final_state.dtype, sshape)
+    if workspace is None:
+        ws, wsb = None, 0
+    else:
+        ws = _check(workspace, "workspace", torch.uint8)
+        wsb = workspace.numel()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    rc = lib.kda_chunk_prefill_fwd(*ptrs, float(lower_bound), float(scale), s0, cu, o, fs, ws,
+                                   ctypes.c_void_p(int(stream)), T, H, N, sdt, wsb)
+    if rc != KDA_OK:
+        detail = lib.kda_last_hip_error().decode() if rc == 4 else ""
+        raise KdaError(rc, f"kda_chunk_prefill_fwd: {kda_status_string(rc)} {detail}".strip())

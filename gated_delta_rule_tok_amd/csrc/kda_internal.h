@@ -1,0 +1,64 @@
+// kda_internal.h -- shared definitions of the gfx950 KDA kernels and the host
+// library that launches them.  Not part of the public ABI (include/kda.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kD = 128;  // head_dim (keys and values)
+constexpr float kNormEps = 1e-6f;
+
+// Everything a kernel needs for one call.  Tensor layouts are those of
+// include/kda.h: q/k/v/g/out [T, H, D] bf16, beta [T, H] bf16, state
+// [N, H, D, D] (row = key channel, column = value channel).
+struct Params {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* g;
+  const uint16_t* beta;
+  const float* A_log;
+  const float* dt_bias;
+  const void* s0;  // may be null (zeros)
+  void* sT;
+  uint16_t* out;
+  const int32_t* cu;
+  int32_t* order;  // sequence processing order (longest first), [N], in the workspace
+  float lower_bound;
+  float scale;
+  int T;           // tokens in q/k/v/g/out (sequence offsets are clamped to it)
+  int H;
+  int N;
+  int vsplit;      // value-dimension slices per (sequence, head)
+  int state_bf16;  // 0: fp32 state, 1: bf16 state
+};
+
+// ---- bf16 helpers (bf16 is the high half of an IEEE fp32) -------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+// ---- launch entry points (one per kernel family) -----------------------------
+
+// Sequence order, longest first (ties by index), into p.order.  One launch.
+hipError_t launch_plan(const Params& p, hipStream_t stream);
+
+// Token-serial fp32 recurrence, one workgroup per (sequence, head, V-slice).
+hipError_t launch_recurrent(const Params& p, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,185 @@
+// kda_recurrent.hip -- token-serial KDA forward in fp32 on the vector ALUs.
+//
+// One workgroup (4 waves) per (sequence, head, value slice).  The slice of the
+// state, 128 key rows x VS value columns in fp32, lives in registers: each lane
+// owns one value column and R = VS/2 consecutive key rows, and the lanes of a
+// wave that share a column are the RG = 256/VS row groups.  Per token:
+//     S <- Diag(a) S;  p = S^T k;  r = S^T (scale q)          (one sweep)
+//     d = beta (v - p);  S <- S + k d^T;  o = r + (k . scale q) d
+// which is the gated delta rule S_t = (I - b k k^T) Diag(a) S_{t-1} + b k v^T,
+// o_t = scale S_t^T q_t with the rank-1 product expanded (the operation of
+// vLLM PR #55737's report, "Features and motivation").  Column sums over the
+// key rows reduce across the RG lanes of a column with cross-lane shuffles, in
+// an order that does not depend on VS.
+//
+// Tokens are taken in blocks of kTB: the four waves first L2-normalise q and k,
+// evaluate the bounded gate a = exp(lb * sigmoid(exp(A_log) (g + dt_bias))) and
+// beta = sigmoid(logit) for the block (one token per wave at a time, two
+// channels per lane) into LDS, then every lane walks the block token by token.
+//
+// Value columns never mix, so any split of the value dimension gives
+// bit-identical results.
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTB = 32;  // tokens staged in LDS per step
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+template <int VS>
+__global__ __launch_bounds__(kThreads) void recurrent_kernel(Params p) {
+  constexpr int CW = VS / 4;   // value columns per wave
+  constexpr int RG = 64 / CW;  // row groups per wave
+  constexpr int R = kD / RG;   // key rows per lane
+  constexpr int GL = R / 8;    // 8-row reduction groups per lane
+  static_assert(R % 8 == 0, "rows per lane must be a multiple of 8");
+
+  __shared__ float s_q[kTB][kD];
+  __shared__ float s_k[kTB][kD];
+  __shared__ float s_a[kTB][kD];
+  __shared__ uint16_t s_v[kTB][VS];  // raw bf16 (keeps the block under 64 KiB of LDS)
+  __shared__ float s_beta[kTB];
+  __shared__ float s_kq[kTB];
+
+  const int slice = blockIdx.x % p.vsplit;
+  const int rest = blockIdx.x / p.vsplit;
+  const int h = rest % p.H;
+  const int n = p.order[rest / p.H];
+  const int H = p.H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane % CW, rg = lane / CW;
+  const int jl = wave * CW + col;  // column inside the slice
+  const int j = slice * VS + jl;   // value channel
+  const int r0 = rg * R;           // first key row
+
+  float S[R];
+  const size_t sbase = ((size_t)n * H + h) * kD * kD;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const size_t idx = sbase + (size_t)(r0 + i) * kD + j;
+    if (!p.s0) S[i] = 0.f;
+    else if (p.state_bf16) S[i] = bf16_to_f32(static_cast<const uint16_t*>(p.s0)[idx]);
+    else S[i] = static_cast<const float*>(p.s0)[idx];
+  }
+
+  const float eA = expf(p.A_log[h]);
+  const float dtb0 = p.dt_bias[h * kD + 2 * lane];
+  const float dtb1 = p.dt_bias[h * kD + 2 * lane + 1];
+  // clamp the sequence to [0, T) so malformed offsets cannot leave the buffers
+  const int bos = min(max(p.cu[n], 0), p.T);
+  const int eos = min(max(p.cu[n + 1], bos), p.T);
+
+  for (int t0 = bos; t0 < eos; t0 += kTB) {
+    const int nt = min(kTB, eos - t0);
+    for (int tt = wave; tt < nt; tt += 4) {
+      const size_t base = ((size_t)(t0 + tt) * H + h) * kD;
+      const uint32_t qp = reinterpret_cast<const uint32_t*>(p.q + base)[lane];
+      const uint32_t kp = reinterpret_cast<const uint32_t*>(p.k + base)[lane];
+      const uint32_t gp = reinterpret_cast<const uint32_t*>(p.g + base)[lane];
+      float q0 = bf16_lo(qp), q1 = bf16_hi(qp);
+      float k0 = bf16_lo(kp), k1 = bf16_hi(kp);
+      const float rq = rsqrtf(wave_sum(q0 * q0 + q1 * q1) + kNormEps) * p.scale;
+      const float rk = rsqrtf(wave_sum(k0 * k0 + k1 * k1) + kNormEps);
+      q0 *= rq; q1 *= rq;
+      k0 *= rk; k1 *= rk;
+      const float kq = wave_sum(q0 * k0 + q1 * k1);
+      const float x0 = eA * (bf16_lo(gp) + dtb0);
+      const float x1 = eA * (bf16_hi(gp) + dtb1);
+      s_q[tt][2 * lane] = q0;
+      s_q[tt][2 * lane + 1] = q1;
+      s_k[tt][2 * lane] = k0;
+      s_k[tt][2 * lane + 1] = k1;
+      s_a[tt][2 * lane] = expf(p.lower_bound / (1.f + expf(-x0)));
+      s_a[tt][2 * lane + 1] = expf(p.lower_bound / (1.f + expf(-x1)));
+      if (lane < VS / 2) {
+        reinterpret_cast<uint32_t*>(&s_v[tt][0])[lane] =
+            reinterpret_cast<const uint32_t*>(p.v + base + slice * VS)[lane];
+      }
+      if (lane == 0) {
+        s_beta[tt] = 1.f / (1.f + expf(-bf16_to_f32(p.beta[(size_t)(t0 + tt) * H + h])));
+        s_kq[tt] = kq;
+      }
+    }
+    __syncthreads();
+
+    for (int tt = 0; tt < nt; ++tt) {
+      // column sums over the 128 key rows in one fixed order for every split:
+      // 16 groups of 8 rows (a sequential FMA chain each), then a pairwise tree
+      // over the group index, low bits first -- the low levels in-lane, the
+      // rest across the lanes of the column (xor shuffles; a+b == b+a exactly)
+      float gk[GL], gq[GL];
+#pragma unroll
+      for (int gi = 0; gi < GL; ++gi) {
+        float ak = 0.f, aq = 0.f;
+#pragma unroll
+        for (int i = gi * 8; i < gi * 8 + 8; i += 4) {
+          const float4 a4 = *reinterpret_cast<const float4*>(&s_a[tt][r0 + i]);
+          const float4 k4 = *reinterpret_cast<const float4*>(&s_k[tt][r0 + i]);
+          const float4 q4 = *reinterpret_cast<const float4*>(&s_q[tt][r0 + i]);
+          S[i] *= a4.x; S[i + 1] *= a4.y; S[i + 2] *= a4.z; S[i + 3] *= a4.w;
+          ak = fmaf(S[i], k4.x, ak); ak = fmaf(S[i + 1], k4.y, ak);
+          ak = fmaf(S[i + 2], k4.z, ak); ak = fmaf(S[i + 3], k4.w, ak);
+          aq = fmaf(S[i], q4.x, aq); aq = fmaf(S[i + 1], q4.y, aq);
+          aq = fmaf(S[i + 2], q4.z, aq); aq = fmaf(S[i + 3], q4.w, aq);
+        }
+        gk[gi] = ak;
+        gq[gi] = aq;
+      }
+#pragma unroll
+      for (int w = 1; w < GL; w *= 2)
+#pragma unroll
+        for (int gi = 0; gi < GL; gi += 2 * w) {
+          gk[gi] += gk[gi + w];
+          gq[gi] += gq[gi + w];
+        }
+      float pk = gk[0], pq = gq[0];
+#pragma unroll
+      for (int m = CW; m < 64; m <<= 1) {
+        pk += __shfl_xor(pk, m, 64);
+        pq += __shfl_xor(pq, m, 64);
+      }
+      const float d = s_beta[tt] * (bf16_to_f32(s_v[tt][jl]) - pk);
+#pragma unroll
+      for (int i = 0; i < R; i += 4) {
+        const float4 k4 = *reinterpret_cast<const float4*>(&s_k[tt][r0 + i]);
+        S[i] = fmaf(k4.x, d, S[i]); S[i + 1] = fmaf(k4.y, d, S[i + 1]);
+        S[i + 2] = fmaf(k4.z, d, S[i + 2]); S[i + 3] = fmaf(k4.w, d, S[i + 3]);
+      }
+      if (rg == 0) p.out[((size_t)(t0 + tt) * H + h) * kD + j] = f32_to_bf16(fmaf(s_kq[tt], d, pq));
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const size_t idx = sbase + (size_t)(r0 + i) * kD + j;
+    if (p.state_bf16) static_cast<uint16_t*>(p.sT)[idx] = f32_to_bf16(S[i]);
+    else static_cast<float*>(p.sT)[idx] = S[i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_recurrent(const Params& p, hipStream_t stream) {
+  const void* fn = nullptr;
+  switch (kD / p.vsplit) {
+    case 128: fn = reinterpret_cast<const void*>(&recurrent_kernel<128>); break;
+    case 64: fn = reinterpret_cast<const void*>(&recurrent_kernel<64>); break;
+    case 32: fn = reinterpret_cast<const void*>(&recurrent_kernel<32>); break;
+    case 16: fn = reinterpret_cast<const void*>(&recurrent_kernel<16>); break;
+    default: return hipErrorInvalidValue;
+  }
+  Params arg = p;
+  void* args[] = {&arg};
+  // the launch status comes from this call alone, not from an earlier runtime call
+  return hipLaunchKernel(fn, dim3(p.N * p.H * p.vsplit), dim3(kThreads), args, 0, stream);
+}
+
+}  // namespace kda

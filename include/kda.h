@@ -1,0 +1,132 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention chunked-prefill
+ * forward library, libkda.so.
+ *
+ * The operation (named in vLLM PR #55737's report, "Use FlashKDA for KDA
+ * chunked prefill", sections "Features and motivation" and "Implementation
+ * breakdown", and its FlashKDA wrapper listing under "Key source snippets"):
+ * for every sequence n delimited by cu_seqlens and every head h, with
+ * head_dim D = 128 and a D x D state S[key c][value j],
+ *
+ *     q_t, k_t  <- x / sqrt(sum_c x[c]^2 + 1e-6)            (L2 norm in-kernel)
+ *     beta_t    =  1 / (1 + exp(-beta_logit_t))              (raw logits in)
+ *     log a_t   =  lower_bound * sigmoid(exp(A_log[h]) * (g_t + dt_bias[h]))
+ *     S_t       =  (I - beta_t k_t k_t^T) Diag(a_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t       =  scale * S_t^T q_t
+ *
+ * starting from initial_state (or zeros) and leaving the last S in
+ * final_state.  The update and output equations are the plain reading of the
+ * gated delta rule the pages name; the gate, the norm, raw beta, the scale on
+ * q, the shapes of A_log ([H]) and dt_bias ([H, D]), the workspace query and
+ * the fp32 / bf16 checkpoint state follow the wrapper listing and PR #56485's
+ * report ("Update flashKDA to support bf16 checkpoint state", "Implementation
+ * breakdown").
+ *
+ * All device pointers are HIP device memory on the current device.  The caller
+ * owns every buffer; the library allocates nothing and keeps no state between
+ * calls except the test-only split override below.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_HEAD_DIM 128
+/* Most negative lower_bound the kernels accept: per-token log-decay is in
+ * [lower_bound, 0], and the chunk kernel factors exp(G_t - G_i) inside 16-token
+ * sub-chunks, whose span must stay inside the fp32 exponent range. */
+#define KDA_LOWER_BOUND_MIN (-5.5f)
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = 1,         /* NULL required pointer, bad size or scalar */
+  KDA_ERR_UNSUPPORTED = 2,         /* lower_bound outside [KDA_LOWER_BOUND_MIN, 0] */
+  KDA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < kda_get_workspace_size(...) */
+  KDA_ERR_HIP = 4                  /* a HIP launch or device query failed */
+} kda_status_t;
+
+typedef enum { KDA_STATE_FP32 = 0, KDA_STATE_BF16 = 1 } kda_state_dtype_t;
+
+/*
+ * Bytes of device workspace kda_chunk_prefill_fwd needs for any call with at
+ * most max_tokens tokens, heads heads and max_seqs sequences (the query the
+ * wrapper listing makes once at construction with max_num_batched_tokens,
+ * local_num_heads, max_num_seqs).  Pure, host-only, monotone in every
+ * argument.  Returns 0 for negative or zero-sized arguments.
+ */
+size_t kda_get_workspace_size(int64_t max_tokens, int32_t heads, int32_t max_seqs);
+
+/*
+ * One KDA chunked-prefill forward over a packed varlen batch.
+ *
+ *   q, k, v, g     bf16 [num_tokens, heads, 128], dense row-major (device)
+ *   beta_logits    bf16 [num_tokens, heads], dense (device); raw logits
+ *   A_log          fp32 [heads] (device)
+ *   dt_bias        fp32 [heads, 128] (device)
+ *   lower_bound    host scalar in [KDA_LOWER_BOUND_MIN, 0]
+ *   scale          host scalar (head_dim^-1/2 in the pages), finite
+ *   initial_state  [num_seqs, heads, 128, 128] in state_dtype, row index = key
+ *                  channel, column = value channel (device); NULL = zeros
+ *   cu_seqlens     int32 [num_seqs + 1] (device): cu[0] = 0, non-decreasing,
+ *                  cu[num_seqs] <= num_tokens.  Read on the device only; its
+ *                  contents are a precondition and are not checked.
+ *   out            bf16 [num_tokens, heads, 128] (device); rows of tokens that
+ *                  belong to a sequence are written (round to nearest even),
+ *                  other rows are not touched
+ *   final_state    [num_seqs, heads, 128, 128] in state_dtype (device); may be
+ *                  the same pointer as initial_state (in-place update), any
+ *                  other overlap is undefined
+ *   workspace      device scratch of workspace_bytes bytes (may be NULL when
+ *                  kda_get_workspace_size(...) is 0)
+ *   stream         hipStream_t to queue the work on (NULL = default stream)
+ *
+ * q, k, v, g, beta_logits and out may be NULL when num_tokens is 0; every other
+ * pointer except initial_state and workspace is required.
+ *
+ * Work is queued on the stream and the call returns without waiting: no host
+ * synchronisation, no allocation and no device-to-host copy, so the call can be
+ * captured into a HIP graph.  All argument checks happen before any HIP call;
+ * on an error nothing is launched.  bf16 state is read by exact widening and
+ * written once, at the end, rounded to nearest even; the state is fp32 in
+ * between.  Results do not depend on the value-dimension split the library
+ * picks (bit-identical).
+ */
+kda_status_t kda_chunk_prefill_fwd(const void* q, const void* k, const void* v, const void* g,
+                                   const void* beta_logits, const float* A_log,
+                                   const float* dt_bias, float lower_bound, float scale,
+                                   const void* initial_state, const int32_t* cu_seqlens, void* out,
+                                   void* final_state, void* workspace, void* stream,
+                                   int64_t num_tokens, int32_t heads, int32_t num_seqs,
+                                   kda_state_dtype_t state_dtype, size_t workspace_bytes);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* kda_status_string(kda_status_t status);
+
+/*
+ * Detail of the most recent KDA_ERR_HIP returned on the calling thread: the HIP
+ * error name and text and the step that failed ("" if there was none).  The
+ * string belongs to the library and stays valid until the next call on this
+ * thread.
+ */
+const char* kda_last_hip_error(void);
+
+/*
+ * Test hook: force the value-dimension split factor (1, 2, 4 or 8; the value
+ * dimension is cut into that many slices, each handled by its own workgroup),
+ * or 0 to let the library choose (the pages' rule: split when
+ * 2 * heads * sequences <= compute units, PR #52458's report, "Features and
+ * motivation").  Process-wide.  Returns the previous setting, or -1 (setting
+ * unchanged) for an invalid value.
+ */
+int kda_debug_set_vsplit(int s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

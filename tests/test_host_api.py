@@ -1,0 +1,137 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+Every call here fails its argument checks before the library makes any HIP
+call, so it runs on a machine without a GPU.  Fake pointers are only ever
+passed together with an argument that is invalid.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_tok_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL, HIPERR = 0, 1, 2, 3, 4
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: each call below is rejected first
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kda.load_library()
+    names = _declared_functions()
+    assert set(names) == {"kda_get_workspace_size", "kda_chunk_prefill_fwd",
+                          "kda_status_string", "kda_last_hip_error", "kda_debug_set_vsplit"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/kda.h but not exported"
+
+
+def test_workspace_size_is_pure_and_monotone():
+    f = kda.kda_get_workspace_size
+    assert f(16384, 16, 8) == f(16384, 16, 8)
+    assert f(-1, 16, 8) == 0 and f(10, 0, 8) == 0 and f(10, 4, 0) == 0
+    prev = 0
+    for n in (1, 2, 8, 64, 1000):
+        cur = f(65536, 32, n)
+        assert cur >= prev
+        prev = cur
+    for t in (0, 1, 64, 65, 16384):
+        assert f(t + 1, 16, 8) >= f(t, 16, 8)
+    for h in (1, 2, 16, 32):
+        assert f(16384, h + 1, 8) >= f(16384, h, 8)
+    assert f(16384, 16, 8) % 256 == 0
+
+
+def test_status_strings():
+    for code in range(5):
+        assert kda.kda_status_string(code).startswith("KDA_")
+    assert kda.kda_status_string(0) == "KDA_OK"
+    assert kda.kda_status_string(99) == "KDA_ERR_UNKNOWN"
+
+
+def test_last_hip_error_empty_without_failures():
+    assert kda.kda_last_hip_error() == ""
+
+
+def test_debug_vsplit_hook():
+    lib = kda.load_library()
+    assert lib.kda_debug_set_vsplit(3) == -1
+    assert lib.kda_debug_set_vsplit(16) == -1
+    prev = lib.kda_debug_set_vsplit(4)
+    assert prev in (0, 1, 2, 4, 8)
+    assert lib.kda_debug_set_vsplit(0) == 4
+    with pytest.raises(ValueError):
+        kda.kda_debug_set_vsplit(5)
+
+
+def _call(**over):
+    """kda_chunk_prefill_fwd through ctypes with valid-looking defaults."""
+    lib = kda.load_library()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE,
+             lb=-5.0, scale=128 ** -0.5, s0=None, cu=FAKE, out=FAKE, sT=FAKE, ws=FAKE,
+             stream=None, T=16384, H=16, N=8, sdt=0, wsb=1 << 20)
+    a.update(over)
+    return lib.kda_chunk_prefill_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["A_log"],
+                                     a["dt_bias"], a["lb"], a["scale"], a["s0"], a["cu"],
+                                     a["out"], a["sT"], a["ws"], a["stream"], a["T"], a["H"],
+                                     a["N"], a["sdt"], a["wsb"])
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "A_log", "dt_bias", "cu", "out",
+                                  "sT"])
+def test_null_required_pointer_rejected(name):
+    assert _call(**{name: None}) == INVALID
+
+
+@pytest.mark.parametrize("over", [
+    dict(T=-1), dict(T=2 ** 31), dict(H=0), dict(H=-3), dict(N=0), dict(N=-1),
+    dict(sdt=2), dict(sdt=-1), dict(lb=float("nan")), dict(lb=float("-inf")),
+    dict(scale=float("inf")), dict(scale=float("nan")), dict(N=2 ** 28, H=16),
+])
+def test_bad_sizes_and_scalars_rejected(over):
+    assert _call(**over) == INVALID
+
+
+@pytest.mark.parametrize("lb", [0.5, 1e-3, -5.6, -100.0])
+def test_lower_bound_outside_range_unsupported(lb):
+    assert _call(lb=lb) == UNSUPPORTED
+
+
+def test_workspace_too_small():
+    need = kda.kda_get_workspace_size(16384, 16, 8)
+    assert need > 0
+    assert _call(wsb=need - 1) == WS_SMALL
+    assert _call(wsb=0) == WS_SMALL
+    # enough bytes claimed but no pointer
+    assert _call(ws=None, wsb=need) == INVALID
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    T, H = 4, 1
+    bf = torch.bfloat16
+    q = torch.zeros(T, H, 128, dtype=bf)
+    with pytest.raises((ValueError, TypeError)):
+        kda.kda_chunk_prefill_fwd(q, q, q, q, torch.zeros(T, H, dtype=bf),
+                                  torch.zeros(H), torch.zeros(H, 128), -5.0, 0.1, None,
+                                  torch.tensor([0, T], dtype=torch.int32), q,
+                                  torch.zeros(1, H, 128, 128), None)
+
+
+def test_one_hip_runtime_in_the_process():
+    """libkda.so must bind to the HIP runtime torch already loaded (same SONAME);
+    a second libamdhip64 in the process sees no device."""
+    kda.load_library()
+    maps = open("/proc/self/maps").read().splitlines()
+    libs = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
+    assert len(libs) == 1, f"more than one HIP runtime mapped: {sorted(libs)}"

@@ -1,0 +1,185 @@
+"""GPU parity: kda_chunk_prefill_fwd (through the C ABI) against the fp64 oracle.
+
+Every output element is compared: out for every token inside a sequence and
+the whole final state, at the five workload shapes and at edge cases.
+
+PYTEST_DONT_REWRITE: failing asserts must not repr device tensors.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import kda_inputs as KI
+from gpu_util import (alloc_outputs, assert_parity, run_gpu, run_oracle, to_device, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def _config(idx):
+    if idx not in _cache:
+        x = KI.config_inputs(idx)
+        print(f"[case] config {idx} {x.meta['config']} T={x.T} H={x.H} N={x.N}", flush=True)
+        _cache[idx] = (x, run_oracle(x))
+    return _cache[idx]
+
+
+@pytest.fixture(autouse=True)
+def _auto_vsplit():
+    import gated_delta_rule_tok_amd as kda
+    kda.kda_debug_set_vsplit(0)
+    yield
+    kda.kda_debug_set_vsplit(0)
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_config_parity(idx):
+    x, (oref, fref) = _config(idx)
+    d = to_device(x)
+    out, fin = run_gpu(x, d)
+    assert_parity(x, out, fin, oref, fref, label=f"config {idx}")
+
+
+@pytest.mark.parametrize("idx", [3, 0, 1])
+def test_vsplit_bit_identical(idx):
+    import torch
+    import gated_delta_rule_tok_amd as kda
+    x, _ = _config(idx)
+    d = to_device(x)
+    res = {}
+    for s in (1, 2, 4, 8):
+        kda.kda_debug_set_vsplit(s)
+        o, f = run_gpu(x, d)
+        torch.cuda.synchronize()
+        res[s] = (o.view(torch.int16).cpu(), f.cpu())
+    for s in (2, 4, 8):
+        assert torch.equal(res[s][0], res[1][0]), f"out differs with split {s}"
+        assert torch.equal(res[s][1], res[1][1]), f"final state differs with split {s}"
+
+
+def test_repeat_calls_bit_identical():
+    import torch
+    x, _ = _config(0)
+    d = to_device(x)
+    o1, f1 = run_gpu(x, d)
+    o2, f2 = run_gpu(x, d)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(f1, f2)
+
+
+def test_null_initial_state_equals_zeros():
+    import torch
+    x = KI.make_inputs([100, 200], 2, seed=31, init_state=None)
+    d = to_device(x)
+    o1, f1 = run_gpu(x, d)
+    z = torch.zeros(2, 2, 128, 128, dtype=torch.float32, device="cuda")
+    o2, f2 = run_gpu(x, d, s0=z)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("state", ["fp32", "bf16"])
+def test_in_place_state_update(state):
+    import torch
+    import gated_delta_rule_tok_amd as kda
+    x = KI.make_inputs([70, 130, 1], 3, seed=32, init_state=state)
+    d = to_device(x)
+    o1, f1 = run_gpu(x, d)
+    s = d["s0"].clone()
+    out, _, ws = alloc_outputs(x, d)
+    kda.kda_chunk_prefill_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"],
+                              d["dt_bias"], x.lower_bound, x.scale, s, d["cu"], out, s, ws)
+    assert torch.equal(out.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(s.view(torch.int16) if state == "bf16" else s,
+                       f1.view(torch.int16) if state == "bf16" else f1)
+
+
+def test_ragged_edges_and_untouched_tail():
+    import torch
+    lengths = [1, 63, 64, 65, 0, 127, 129, 5, 192, 2]
+    x = KI.make_inputs(lengths, 3, seed=33, init_state="fp32", extra_tokens=7)
+    print(f"[case] ragged {lengths} + 7 tail tokens, H=3", flush=True)
+    d = to_device(x)
+    out, fin, ws = alloc_outputs(x, d, fill_out=0x7FC1)  # NaN sentinel
+    run_gpu(x, d, out, fin, ws)
+    oref, fref = run_oracle(x)
+    assert_parity(x, out, fin, oref, fref, label="ragged")
+    tail = out.view(torch.int16)[int(x.cu_seqlens[-1]):]
+    assert bool((tail == 0x7FC1).all()), "rows past the last sequence were written"
+    # the empty sequence keeps its initial state exactly
+    assert torch.equal(fin[4], d["s0"][4])
+
+
+@pytest.mark.parametrize("state", ["fp32", "bf16"])
+def test_zero_tokens_keeps_state(state):
+    import torch
+    x = KI.make_inputs([0, 0, 0], 2, seed=34, init_state=state)
+    d = to_device(x)
+    out, fin = run_gpu(x, d)
+    torch.cuda.synchronize()
+    a = fin.view(torch.int16) if state == "bf16" else fin
+    b = d["s0"].view(torch.int16) if state == "bf16" else d["s0"]
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("lb", [0.0, -1.0, -5.5])
+def test_lower_bound_range(lb):
+    x = KI.make_inputs([150, 66], 2, seed=35, init_state="fp32", lower_bound=lb)
+    d = to_device(x)
+    out, fin = run_gpu(x, d)
+    oref, fref = run_oracle(x)
+    assert_parity(x, out, fin, oref, fref, label=f"lb={lb}")
+
+
+def test_bf16_state_small():
+    x = KI.make_inputs([300, 45, 64], 4, seed=36, init_state="bf16")
+    d = to_device(x)
+    out, fin = run_gpu(x, d)
+    oref, fref = run_oracle(x)
+    assert_parity(x, out, fin, oref, fref, label="bf16 state")
+
+
+def test_graph_capture_replay_matches_eager():
+    import torch
+    x = KI.make_inputs([200, 64, 300], 4, seed=37, init_state="fp32")
+    d = to_device(x)
+    eo, ef = run_gpu(x, d)
+    torch.cuda.synchronize()
+    out, fin, ws = alloc_outputs(x, d)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            run_gpu(x, d, out, fin, ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        fin.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eo.view(torch.int16)), f"replay {rep} out"
+        assert torch.equal(fin, ef), f"replay {rep} final state"
+        run_gpu(x, d)  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_invalid_arguments_raise():
+    import torch
+    import gated_delta_rule_tok_amd as kda
+    x = KI.make_inputs([10], 1, seed=38, init_state="fp32")
+    d = to_device(x)
+    out, fin, ws = alloc_outputs(x, d)
+    with pytest.raises(kda.KdaError) as e:
+        kda.kda_chunk_prefill_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"],
+                                  d["dt_bias"], 0.5, x.scale, d["s0"], d["cu"], out, fin, ws)
+    assert e.value.status == 2
+    with pytest.raises(TypeError):
+        kda.kda_chunk_prefill_fwd(d["q"].float(), d["k"], d["v"], d["g"], d["beta"], d["A_log"],
+                                  d["dt_bias"], -5.0, x.scale, d["s0"], d["cu"], out, fin, ws)
+    small = torch.empty(0, dtype=torch.uint8, device="cuda")
+    with pytest.raises(kda.KdaError) as e:
+        kda.kda_chunk_prefill_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"],
+                                  d["dt_bias"], -5.0, x.scale, d["s0"], d["cu"], out, fin, small)
+    assert e.value.status == 3
