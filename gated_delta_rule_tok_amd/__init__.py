@@ -15,7 +15,7 @@ import ctypes
 import os
 
 __all__ = ["kda_get_workspace_size", "kda_chunk_prefill_fwd", "kda_status_string",
-           "kda_last_hip_error", "kda_debug_set_vsplit", "KdaError", "library_path", "load_library"]
+           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel", "KdaError", "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -70,6 +70,8 @@ def load_library():
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_last_hip_error.argtypes = []
         lib.kda_last_hip_error.restype = ctypes.c_char_p
+        lib.kda_debug_set_kernel.argtypes = [ctypes.c_int]
+        lib.kda_debug_set_kernel.restype = ctypes.c_int
         lib.kda_debug_set_vsplit.argtypes = [ctypes.c_int]
         lib.kda_debug_set_vsplit.restype = ctypes.c_int
         _lib = lib
@@ -86,6 +88,14 @@ def kda_status_string(status: int) -> str:
 
 def kda_last_hip_error() -> str:
     return load_library().kda_last_hip_error().decode()
+
+
+def kda_debug_set_kernel(k: int) -> int:
+    """Test hook: 0/1 chunked MFMA kernel (default), 2 token-serial kernel."""
+    prev = load_library().kda_debug_set_kernel(int(k))
+    if prev < 0:
+        raise ValueError(f"invalid kernel selector {k}")
+    return prev
 
 
 def kda_debug_set_vsplit(s: int) -> int:

@@ -23,6 +23,7 @@ constexpr size_t kAlign = 256;
 constexpr int kMaxDevices = 64;
 
 std::atomic<int> g_vsplit_override{0};
+std::atomic<int> g_kernel_override{0};
 std::atomic<int> g_cu_count[kMaxDevices];
 
 thread_local char t_last_hip_error[256] = "";
@@ -90,6 +91,11 @@ const char* kda_status_string(kda_status_t status) {
 
 const char* kda_last_hip_error(void) { return t_last_hip_error; }
 
+int kda_debug_set_kernel(int k) {
+  if (k < 0 || k > 2) return -1;
+  return g_kernel_override.exchange(k);
+}
+
 int kda_debug_set_vsplit(int s) {
   if (!(s == 0 || s == 1 || s == 2 || s == 4 || s == 8)) return -1;
   return g_vsplit_override.exchange(s);
@@ -146,8 +152,13 @@ kda_status_t kda_chunk_prefill_fwd(const void* q, const void* k, const void* v, 
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (hipError_t e = kda::launch_plan(p, st); e != hipSuccess) return hip_failure(e, "plan launch");
-  if (hipError_t e = kda::launch_recurrent(p, st); e != hipSuccess)
-    return hip_failure(e, "recurrent launch");
+  if (g_kernel_override.load(std::memory_order_relaxed) == 2) {
+    if (hipError_t e = kda::launch_recurrent(p, st); e != hipSuccess)
+      return hip_failure(e, "token-serial kernel launch");
+  } else {
+    if (hipError_t e = kda::launch_chunk(p, st); e != hipSuccess)
+      return hip_failure(e, "chunk kernel launch");
+  }
   return KDA_OK;
 }
 

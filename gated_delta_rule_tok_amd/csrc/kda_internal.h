@@ -61,4 +61,8 @@ hipError_t launch_plan(const Params& p, hipStream_t stream);
 // Token-serial fp32 recurrence, one workgroup per (sequence, head, V-slice).
 hipError_t launch_recurrent(const Params& p, hipStream_t stream);
 
+// Chunked (64-token WY/UT) forward with bf16 MFMA, one workgroup per
+// (sequence, head, V-slice).
+hipError_t launch_chunk(const Params& p, hipStream_t stream);
+
 }  // namespace kda

@@ -84,9 +84,17 @@ def diff_stats(gpu: np.ndarray, ref: np.ndarray) -> dict:
                 rel_rms=float(np.sqrt((d * d).sum() / max((ref * ref).sum(), 1e-300))))
 
 
-def assert_parity(x: KI.KdaInputs, out_gpu, fin_gpu, out_ref, fin_ref, label="", rows=None):
+# Relative bounds for inputs whose state grows far beyond the workloads' scale
+# (weak or no decay): bf16 operands give ~2^-9 relative error per product.
+REL_RMS_OUT = 5e-3
+REL_RMS_STATE = 3e-3
+
+
+def assert_parity(x: KI.KdaInputs, out_gpu, fin_gpu, out_ref, fin_ref, label="", rows=None,
+                  relative=False):
     """max|d| and mean|d| bounds on out (rows of tokens inside sequences) and on
-    the final state."""
+    the final state.  relative=True keeps the max|d| bound and replaces the
+    absolute mean|d| bound by relative-RMS bounds."""
     tol = MAX_ABS_BF16_STATE if x.state_bf16 else MAX_ABS_FP32_STATE
     if rows is None:
         rows = np.concatenate([np.arange(x.cu_seqlens[i], x.cu_seqlens[i + 1])
@@ -94,6 +102,10 @@ def assert_parity(x: KI.KdaInputs, out_gpu, fin_gpu, out_ref, fin_ref, label="",
     so = diff_stats(to_f64(out_gpu)[rows], out_ref[rows])
     sf = diff_stats(to_f64(fin_gpu), fin_ref)
     print(f"[parity] {label} out {so} final {sf}", flush=True)
+    if relative:
+        assert so["max_abs"] <= tol and so["rel_rms"] <= REL_RMS_OUT, f"{label} out: {so}"
+        assert sf["max_abs"] <= tol and sf["rel_rms"] <= REL_RMS_STATE, f"{label} final: {sf}"
+        return so, sf
     assert so["max_abs"] <= tol and so["mean_abs"] <= MEAN_ABS, f"{label} out: {so}"
     assert sf["max_abs"] <= tol and sf["mean_abs"] <= MEAN_ABS, f"{label} final state: {sf}"
     return so, sf

@@ -31,7 +31,8 @@ def test_library_exports_every_declared_symbol():
     lib = kda.load_library()
     names = _declared_functions()
     assert set(names) == {"kda_get_workspace_size", "kda_chunk_prefill_fwd",
-                          "kda_status_string", "kda_last_hip_error", "kda_debug_set_vsplit"}
+                          "kda_status_string", "kda_last_hip_error", "kda_debug_set_vsplit",
+                          "kda_debug_set_kernel"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/kda.h but not exported"
 

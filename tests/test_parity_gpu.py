@@ -122,13 +122,25 @@ def test_zero_tokens_keeps_state(state):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("lb", [0.0, -1.0, -5.5])
+@pytest.mark.parametrize("lb", [-1.0, -5.5])
 def test_lower_bound_range(lb):
     x = KI.make_inputs([150, 66], 2, seed=35, init_state="fp32", lower_bound=lb)
     d = to_device(x)
     out, fin = run_gpu(x, d)
     oref, fref = run_oracle(x)
     assert_parity(x, out, fin, oref, fref, label=f"lb={lb}")
+
+
+@pytest.mark.parametrize("lb", [0.0, -0.05])
+def test_weak_or_no_decay(lb):
+    """Without decay the state keeps growing (|S| ~8x the workloads' scale at
+    216 tokens), so the absolute mean bound calibrated on the workloads does not
+    apply; the max bound does, and the error stays at bf16 relative precision."""
+    x = KI.make_inputs([150, 66], 2, seed=35, init_state="fp32", lower_bound=lb)
+    d = to_device(x)
+    out, fin = run_gpu(x, d)
+    oref, fref = run_oracle(x)
+    assert_parity(x, out, fin, oref, fref, label=f"lb={lb}", relative=True)
 
 
 def test_bf16_state_small():
@@ -183,3 +195,17 @@ def test_invalid_arguments_raise():
         kda.kda_chunk_prefill_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"],
                                   d["dt_bias"], -5.0, x.scale, d["s0"], d["cu"], out, fin, small)
     assert e.value.status == 3
+
+
+@pytest.mark.parametrize("idx", [0, 3])
+def test_token_serial_kernel_parity(idx):
+    """The second, token-serial GPU implementation also matches the oracle."""
+    import gated_delta_rule_tok_amd as kda
+    x, (oref, fref) = _config(idx)
+    d = to_device(x)
+    prev = kda.kda_debug_set_kernel(2)
+    try:
+        out, fin = run_gpu(x, d)
+    finally:
+        kda.kda_debug_set_kernel(prev)
+    assert_parity(x, out, fin, oref, fref, label=f"token-serial config {idx}")
