@@ -132,7 +132,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": x.meta["config"], "tokens": T, "sequences": N, "heads": H,
                    "head_dim": 128, "state": "bf16" if x.state_bf16 else "fp32",
