@@ -30,6 +30,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "KDA prefill tokens/s + µs/layer (8x2048, H=16, D=128); % of MFMA/HBM roofline"
+CSRC = os.path.join(ROOT, "gated_delta_rule_tok_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, AMD spec
 MFMA_BF16_PEAK_TF = 2500.0  # dense bf16, AMD spec
 
@@ -42,6 +44,56 @@ def algorithmic_bytes(T, H, N, state_bytes, has_initial):
     return T * H * per_token_head + N * H * per_seq_head
 
 
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources; traffic figures are only valid for the
+    sources they were measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"traffic__chunk_kernel__{workload}.json")
+
+
+def _pmc_sum(path: str, kernel_sub: str):
+    """Mean over dispatches of the per-dispatch counter sum, for one kernel."""
+    import collections
+    import csv
+    per = collections.defaultdict(float)
+    for r in csv.DictReader(open(path)):
+        if kernel_sub in r["Kernel_Name"]:
+            per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return (sum(per.values()) / len(per), len(per)) if per else (None, 0)
+
+
+def traffic_from_pmc(pmc_dir: str, workload: str, command: str) -> dict:
+    """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) of the
+    benchmark and of a plain device copy of known size into HBM bytes per
+    launch of the chunk kernel.  Expects pmc_dir/{fetch,write,cal_fetch,cal_write}/
+    run_counter_collection.csv; the calibration copy moves 256 MiB."""
+    f = lambda d: os.path.join(pmc_dir, d, "run_counter_collection.csv")
+    fetch, nf = _pmc_sum(f("fetch"), "chunk_kernel")
+    write, nw = _pmc_sum(f("write"), "chunk_kernel")
+    cal_f, _ = _pmc_sum(f("cal_fetch"), "copyBuffer")
+    cal_w, _ = _pmc_sum(f("cal_write"), "copyBuffer")
+    copy_kib = 256 * 1024
+    fs, ws = copy_kib / cal_f, copy_kib / cal_w
+    out = {"kernel_source_sha256": kernel_source_hash(), "workload": workload,
+           "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+           "dispatches": [nf, nw], "fetch_scale": fs, "write_scale": ws,
+           "calibration": "device copy of 256 MiB: FETCH_SIZE %.0f KiB, WRITE_SIZE %.0f KiB"
+                          % (cal_f, cal_w),
+           "bytes_per_launch": (fetch * fs + write * ws) * 1024.0,
+           "read_bytes": fetch * fs * 1024.0, "write_bytes": write * ws * 1024.0,
+           "command": command}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -50,7 +102,22 @@ def main():
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--sets", type=int, default=2, help="buffer sets rotated across steps")
+    ap.add_argument("--traffic-from", metavar="PMC_DIR",
+                    help="write the traffic file for --config from rocprofv3 counter runs, then exit")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        import kda_inputs as KI
+        wl = KI.CONFIGS[args.config]["name"]
+        cmd = ("for c in FETCH_SIZE WRITE_SIZE: rocprofv3 --pmc $c --output-format csv -- "
+               f"python bench.py --config {args.config} --steps 3 --warmup 1 --no-cpu; the same "
+               "counters over a 256 MiB device copy for calibration")
+        t = traffic_from_pmc(args.traffic_from, wl, cmd)
+        os.makedirs(PROFILES, exist_ok=True)
+        with open(traffic_file(wl), "w") as fh:
+            json.dump(t, fh, indent=1)
+        print(json.dumps(t))
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
@@ -119,6 +186,13 @@ def main():
     abytes = algorithmic_bytes(T, H, N, sbytes, x.initial_state is not None)
     achieved_gbs = abytes / (launch_ms * 1e-3) / 1e9
 
+    traffic = None
+    tf = traffic_file(x.meta["config"])
+    if os.path.exists(tf):
+        t = json.load(open(tf))
+        if t.get("kernel_source_sha256") == kernel_source_hash():
+            traffic = t["bytes_per_launch"]
+
     result = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -138,7 +212,7 @@ def main():
                    "head_dim": 128, "state": "bf16" if x.state_bf16 else "fp32",
                    "initial_state": x.initial_state is not None, "buffer_sets": len(sets)},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": abytes, "launch_us": launch_ms * 1e3},
     }
 

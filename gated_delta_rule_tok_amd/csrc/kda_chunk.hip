@@ -34,11 +34,18 @@
 // sub-chunks use the later sub-chunk's reference and an extra per-channel
 // factor e^{R_a - R_b} <= 1 on the earlier sub-chunk's operand.
 //
-// MFMA layout facts used here (v_mfma_f32_16x16x32_bf16 and
-// v_mfma_f32_16x16x16_bf16): lane l holds accumulator rows 4*(l/16)+j of
-// column l%16.  Operand k-slots only have to agree between A and B, so a
-// k-block of 32 built from two accumulator tiles uses the slot order
-// {4g..4g+3, 16+4g..16+4g+3} (g = l/16) on both sides.
+// gfx950 facts used here, each checked on the device:
+//  * v_mfma_f32_16x16x{32,16}_bf16: lane l holds accumulator rows 4*(l/16)+j of
+//    column l%16.  Operand k-slots only have to agree between A and B, so a
+//    k-block of 32 built from two accumulator tiles uses the slot order
+//    {4g..4g+3, 16+4g..16+4g+3} (g = l/16) on both sides.
+//  * ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4 of
+//    the 8-byte loads of lanes i/4, 4+i/4, 8+i/4, 12+i/4.  With lane L pointing
+//    at row base+L/4, columns c0+4*(L%4).., lane i gets column c0+i of rows
+//    base..base+3 -- an operand with k running over rows, read straight from a
+//    row-major [token][channel] array.  So every operand stays row-major.
+//  * v_permlane16_swap / v_permlane32_swap exchange 16-lane rows and 32-lane
+//    halves; they carry the cumulative-sum scan across the rows of a wave.
 #include "kda_internal.h"
 
 namespace kda {
@@ -47,12 +54,20 @@ namespace {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kC = 64;  // tokens per chunk
 constexpr float kLog2e = 1.4426950408889634f;
+
+// LDS row strides in bf16 elements, chosen for the access each array sees:
+constexpr int kRowA = 136;  // 68 dwords = 4 mod 32: 16-row 16-byte operand reads
+constexpr int kRowT = 144;  // 72 dwords = 8 mod 32: transpose reads (4 rows x 32 B)
+constexpr int kRowW = 132;  // 66 dwords = 2 mod 32: 16-row 8-byte operand reads
+constexpr int kRowM = 68;   // 64 x 64 token-token matrices read 8 bytes per row
+constexpr int kRowL = 72;   // 64 x 64 read 16 bytes per row
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -73,79 +88,50 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
 __device__ __forceinline__ f32x4 to_f32x4(bf16x4 v) {
   return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
-
-// Blocks (a, b), b <= a, of the 4 x 4 block-lower-triangular chunk matrices.
-__device__ __forceinline__ int blk(int a, int b) { return a * (a + 1) / 2 + b; }
-
-template <int VS>
-struct Smem {
-  union {
-    bf16 ke[kC][136];  // k^ e^{G-R}, rows = tokens (A left operand)
-    struct {
-      bf16 row[10][16][24];  // triangular-inverse blocks, row-major
-      bf16 col[10][16][24];  // the same blocks transposed
-    } tb;
-    bf16 wn[kC][136];  // -W, rows = tokens
-  } r0;
-  bf16 qe[kC][136];     // (scale q^) e^{G-R}; later e^G (scale q^)
-  bf16 kf[kC][136];     // k^ e^{R-G} (A/Mq right operand)
-  bf16 xwt[128][72];    // e^G k^, [channel][token]
-  bf16 kph[128][72];    // e^{G_last-G} k^, high bf16 part, [channel][token]
-  bf16 kpl[128][72];    // low part
-  float adiag[4][16][20];  // diagonal 16x16 blocks of A (fp32)
-  bf16 aoff[kC][72];    // off-diagonal blocks of A; later Mq
-  bf16 lb[kC][72];      // L = (Tm - I) diag(b), [token][token]
-  bf16 vt[VS][72];      // V slice, [column][token]
-  float beta[kC];
-  float rloc[4][128];   // G at token 7 of each sub-chunk, relative to the sub-chunk
-  float wtot[4][128];   // per-sub-chunk totals of the log-decay
-  float dab[6][128];    // e^{R_a - R_b}, a > b
-  float gam[128];       // e^{G_last}
-};
-
-// Global-memory values of one chunk, loaded one chunk ahead into registers.
-// Thread (tq, co) = (tid / 16, tid % 16) covers tokens 4tq..4tq+3 and key
-// channels 8co..8co+7 (q, k, g), and value columns co*VS/16 .. +VS/16-1.
-template <int VS>
-struct Prefetch {
-  static constexpr int VN = VS / 16;  // value columns per thread
-  uint4 q[4], k[4], g[4];
-  bf16 v[4][VN];
-  float beta;
-};
-
-template <int VS>
-__device__ __forceinline__ void load_chunk(Prefetch<VS>& pf, const Params& p, int h, int slice,
-                                           int t0, int L, int tq, int co, int tid) {
-  const int H = p.H;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = 4 * tq + r;
-    if (t < L) {
-      const size_t base = ((size_t)(t0 + t) * H + h) * kD;
-      pf.q[r] = *reinterpret_cast<const uint4*>(p.q + base + 8 * co);
-      pf.k[r] = *reinterpret_cast<const uint4*>(p.k + base + 8 * co);
-      pf.g[r] = *reinterpret_cast<const uint4*>(p.g + base + 8 * co);
-      const bf16* vp = reinterpret_cast<const bf16*>(p.v + base + slice * VS + co * Prefetch<VS>::VN);
-#pragma unroll
-      for (int c = 0; c < Prefetch<VS>::VN; ++c) pf.v[r][c] = vp[c];
-    } else {
-      pf.q[r] = pf.k[r] = pf.g[r] = uint4{0, 0, 0, 0};
-#pragma unroll
-      for (int c = 0; c < Prefetch<VS>::VN; ++c) pf.v[r][c] = (bf16)0.f;
-    }
-  }
-  pf.beta = (tid < L) ? bf16_to_f32(p.beta[(size_t)(t0 + tid) * H + h]) : 0.f;
+__device__ __forceinline__ bf16x8 pack8(const float* f) {
+  return bf16x8{(bf16)f[0], (bf16)f[1], (bf16)f[2], (bf16)f[3],
+                (bf16)f[4], (bf16)f[5], (bf16)f[6], (bf16)f[7]};
 }
-
 __device__ __forceinline__ void unpack8(uint4 u, float* f) {
   f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
   f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
 }
 
-__device__ __forceinline__ bf16x8 pack8(const float* f) {
-  return bf16x8{(bf16)f[0], (bf16)f[1], (bf16)f[2], (bf16)f[3],
-                (bf16)f[4], (bf16)f[5], (bf16)f[6], (bf16)f[7]};
+// Sum over the 16 lanes of a DPP row (all 16 lanes get the same bits).
+__device__ __forceinline__ float row_sum16(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+// Exclusive prefix sum over the four 16-lane rows of a wave (per lane column).
+__device__ __forceinline__ float rows_exclusive_sum(float x, int row) {
+  const uint32_t u = __float_as_uint(x);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float from_prev_row = __uint_as_float(s16[0]);  // odd rows: row - 1
+  const float from_next_row = __uint_as_float(s16[1]);  // even rows: row + 1
+  const bool odd = row & 1;
+  const float pair = x + (odd ? from_prev_row : from_next_row);  // t0+t1 or t2+t3
+  const uint32_t up = __float_as_uint(pair);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(up, up, false, false);
+  const float low_pair = __uint_as_float(s32[0]);  // rows 2, 3: t0 + t1
+  return (odd ? from_prev_row : 0.f) + (row >= 2 ? low_pair : 0.f);
+}
+
+// Transposed 8-byte LDS read (see the header comment): pointer of this lane.
+__device__ __forceinline__ bf16x4 tr4(const bf16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// Operand with k over 4 consecutive rows base.. and lane column c0 + l16 of a
+// row-major array: the transpose read with lane L at row base + L/4.
+template <int STRIDE>
+__device__ __forceinline__ bf16x4 rows4(const bf16 (*arr)[STRIDE], int base, int c0, int l16) {
+  return tr4(&arr[base + (l16 >> 2)][c0 + 4 * (l16 & 3)]);
 }
 
 // A-operand rows for a k-block of 32 whose B operand was built from two
@@ -157,15 +143,108 @@ __device__ __forceinline__ bf16x8 perm_row(const bf16 (*arr)[STRIDE], int row, i
   return cat(lo, hi);
 }
 
+// Pair index -> block (a, b), b <= a, of the 4 x 4 sub-chunk blocks.
+__device__ __forceinline__ void pair_ab(int pi, int& a, int& b) {
+  a = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
+  b = pi - (a * (a + 1)) / 2;
+}
+
+template <int VS>
+struct Smem {
+  static constexpr int VROW = VS + 16 > 48 ? VS + 16 : 48;  // transpose reads
+  bf16 ke[kC][kRowA];   // k^ e^{G-R} (A left operand); then e^G k^ (W right operand)
+  bf16 qe[kC][kRowA];   // (scale q^) e^{G-R} (Mq left); then e^G (scale q^) (O left)
+  union {
+    bf16 kf[kC][kRowA];  // k^ e^{R-G} (A / Mq right operand)
+    struct {
+      bf16 row[4][16][24];  // diagonal inverse blocks D_a, row-major
+      bf16 col[4][16][24];  // the same, transposed
+    } d;
+    bf16 wn[kC][kRowW];  // -W
+  } r2;
+  bf16 kph[kC][kRowT];  // e^{G_last-G} k^, high bf16 part
+  bf16 kpl[kC][kRowT];  // low part
+  bf16 v[kC][VROW];     // value slice [token][column]
+  float adt[4][16][20];  // diagonal blocks of A, transposed: adt[a][m][r] = A[16a+r][16a+m]
+  bf16 aoff[kC][kRowM];  // off-diagonal blocks of A; then Mq
+  bf16 lb[kC][kRowL];    // L = (Tm - I) diag(b)
+  float beta[kC];
+  float rloc[4][128];   // G at token 7 of each sub-chunk, relative to the sub-chunk start
+  float wtot[4][128];   // log-decay total of each sub-chunk
+  float dab[6][128];    // e^{R_a - R_b}, a > b
+  float gam[128];       // e^{G_last}
+};
+
+// Global values of one chunk, fetched one chunk ahead.  Thread (tq, co) =
+// (tid / 16, tid % 16) covers tokens 4tq..4tq+3, key channels 8co..8co+7 and
+// value columns co*VN..co*VN+VN-1 of the slice.
+template <int VS>
+struct Prefetch {
+  static constexpr int VN = VS / 16;
+  uint4 q[4], k[4], g[4];
+  bf16 v[4][VN];
+  float beta;
+};
+
+template <int VS>
+__device__ __forceinline__ void load_row(Prefetch<VS>& pf, int r, const uint16_t* q, const uint16_t* k,
+                                         const uint16_t* g, const uint16_t* v) {
+  constexpr int VN = Prefetch<VS>::VN;
+  pf.q[r] = *reinterpret_cast<const uint4*>(q);
+  pf.k[r] = *reinterpret_cast<const uint4*>(k);
+  pf.g[r] = *reinterpret_cast<const uint4*>(g);
+  const bf16* vp = reinterpret_cast<const bf16*>(v);
+  if constexpr (VN == 8) {
+    *reinterpret_cast<bf16x8*>(pf.v[r]) = *reinterpret_cast<const bf16x8*>(vp);
+  } else if constexpr (VN == 4) {
+    *reinterpret_cast<bf16x4*>(pf.v[r]) = *reinterpret_cast<const bf16x4*>(vp);
+  } else {
+#pragma unroll
+    for (int c = 0; c < VN; ++c) pf.v[r][c] = vp[c];
+  }
+}
+
+// Fetch chunk [t0, t0 + L).  Offsets are 32-bit from per-call base pointers
+// (q/k/g/v already point at this thread's channels of token 0, head h).
+template <int VS>
+__device__ __forceinline__ void load_chunk(Prefetch<VS>& pf, const uint16_t* q, const uint16_t* k,
+                                           const uint16_t* g, const uint16_t* v,
+                                           const uint16_t* beta, int rowstride, int H, int t0,
+                                           int L, int tq, int tid) {
+  constexpr int VN = Prefetch<VS>::VN;
+  if (L == kC) {  // full chunk: no per-row predicates
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const unsigned off = (unsigned)(t0 + 4 * tq + r) * (unsigned)rowstride;
+      load_row<VS>(pf, r, q + off, k + off, g + off, v + off);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * tq + r;
+      if (t < L) {
+        const unsigned off = (unsigned)(t0 + t) * (unsigned)rowstride;
+        load_row<VS>(pf, r, q + off, k + off, g + off, v + off);
+      } else {
+        pf.q[r] = pf.k[r] = pf.g[r] = uint4{0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < VN; ++c) pf.v[r][c] = (bf16)0.f;
+      }
+    }
+  }
+  pf.beta = (tid < L) ? bf16_to_f32(beta[(unsigned)(t0 + tid) * (unsigned)H]) : 0.f;
+}
+
 template <int VS>
 __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
-  constexpr int NS = VS / 16;                 // 16-column strips in the slice
-  constexpr int SPW = NS >= 4 ? NS / 4 : 1;   // strips per wave
+  constexpr int NS = VS / 16;                // 16-column strips in the slice
+  constexpr int SPW = NS >= 4 ? NS / 4 : 1;  // strips per wave
+  constexpr int VN = Prefetch<VS>::VN;
   __shared__ __attribute__((aligned(16))) Smem<VS> sm;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g4 = lane >> 4;  // MFMA lane coordinates
-  const int tq = tid >> 4, co = tid & 15;     // elementwise coordinates
+  const int tq = tid >> 4, co = tid & 15;     // elementwise coordinates (g4 = tq % 4)
   const int ch0 = 8 * co;
 
   // workgroup -> (sequence rank, head, slice); consecutive work items (the
@@ -180,12 +259,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
   const int H = p.H;
 
   // zero the triangular buffers whose upper blocks are never written
-  for (int i = tid; i < kC * 72 / 8; i += kThreads) {
-    reinterpret_cast<uint4*>(&sm.lb[0][0])[i] = uint4{0, 0, 0, 0};
+  for (int i = tid; i < kC * kRowM / 8; i += kThreads)
     reinterpret_cast<uint4*>(&sm.aoff[0][0])[i] = uint4{0, 0, 0, 0};
-  }
+  for (int i = tid; i < kC * kRowL / 8; i += kThreads)
+    reinterpret_cast<uint4*>(&sm.lb[0][0])[i] = uint4{0, 0, 0, 0};
 
-  // per-head constants: sigmoid argument in log2 units, lower bound in log2
+  // per-head constants: sigmoid argument and lower bound in log2 units
   const float eA = expf(p.A_log[h]);
   const float c1 = -kLog2e * eA;
   float c2[8];
@@ -193,8 +272,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
   for (int i = 0; i < 8; ++i) c2[i] = c1 * p.dt_bias[h * kD + ch0 + i];
   const float lb2 = p.lower_bound * kLog2e;
 
-  // state slice in accumulator layout: strip s, row tile rt, element j ->
-  // S[16 rt + 4 g4 + j][16 s + l16] of this slice
+  // state slice in accumulator layout: S[st][rt][j] = S[16 rt + 4 g4 + j][16 s + l16]
   f32x4 S[SPW][8];
   const size_t sbase = ((size_t)n * H + h) * kD * kD;
 #pragma unroll
@@ -218,8 +296,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
   const int bos = min(max(p.cu[n], 0), p.T);
   const int eos = min(max(p.cu[n + 1], bos), p.T);
 
+  // base pointers of token 0 for this head (and this thread's channels);
+  // per-token offsets below are 32-bit (T * H * 128 < 2^31 elements is checked on the host)
+  const int rowstride = H * kD;
+  const uint16_t* qb = p.q + (size_t)h * kD + 8 * co;
+  const uint16_t* kb = p.k + (size_t)h * kD + 8 * co;
+  const uint16_t* gb = p.g + (size_t)h * kD + 8 * co;
+  const uint16_t* vb = p.v + (size_t)h * kD + slice * VS + co * VN;
+  const uint16_t* betab = p.beta + h;
+  uint16_t* outb = p.out + (size_t)h * kD + slice * VS;
+
   Prefetch<VS> pf;
-  if (bos < eos) load_chunk<VS>(pf, p, h, slice, bos, min(kC, eos - bos), tq, co, tid);
+  if (bos < eos) load_chunk<VS>(pf, qb, kb, gb, vb, betab, rowstride, H, bos, min(kC, eos - bos), tq, tid);
 
   for (int t0 = bos; t0 < eos; t0 += kC) {
     const int L = min(kC, eos - t0);
@@ -232,17 +320,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
       unpack8(pf.q[r], qf[r]);
       unpack8(pf.k[r], kf[r]);
       unpack8(pf.g[r], lam[r]);
-    }
-    // value slice -> vt[column][token]; beta
 #pragma unroll
-    for (int c = 0; c < Prefetch<VS>::VN; ++c) {
-      bf16x4 v4 = {pf.v[0][c], pf.v[1][c], pf.v[2][c], pf.v[3][c]};
-      *reinterpret_cast<bf16x4*>(&sm.vt[co * Prefetch<VS>::VN + c][4 * tq]) = v4;
+      for (int c = 0; c < VN; ++c) sm.v[4 * tq + r][co * VN + c] = pf.v[r][c];
     }
     if (tid < kC) sm.beta[tid] = tid < L ? rcp(1.f + ex2(-kLog2e * pf.beta)) : 0.f;
 
     // the registers are free again: fetch the next chunk behind this one's compute
-    if (t0 + kC < eos) load_chunk<VS>(pf, p, h, slice, t0 + kC, min(kC, eos - t0 - kC), tq, co, tid);
+    if (t0 + kC < eos)
+      load_chunk<VS>(pf, qb, kb, gb, vb, betab, rowstride, H, t0 + kC, min(kC, eos - t0 - kC), tq, tid);
 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -252,13 +337,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
         qq = fmaf(qf[r][i], qf[r][i], qq);
         kk = fmaf(kf[r][i], kf[r][i], kk);
       }
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-        qq += __shfl_xor(qq, m, 16);
-        kk += __shfl_xor(kk, m, 16);
-      }
-      const float rq = rsqrtf(qq + kNormEps) * p.scale;
-      const float rk = rsqrtf(kk + kNormEps);
+      const float rq = rsqrtf(row_sum16(qq) + kNormEps) * p.scale;
+      const float rk = rsqrtf(row_sum16(kk) + kNormEps);
       const bool valid = 4 * tq + r < L;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -269,45 +349,69 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
         lam[r][i] = valid ? lb2 * rcp(1.f + e) : 0.f;
       }
     }
-    // inclusive cumulative sum over the chunk's tokens, per channel
+    // inclusive cumulative sum from the start of this wave's 16-token sub-chunk
 #pragma unroll
     for (int r = 1; r < 4; ++r)
 #pragma unroll
       for (int i = 0; i < 8; ++i) lam[r][i] += lam[r - 1][i];
-    float rloc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float tot = lam[3][i];
-      float x = tot;
-      float y = __shfl_up(x, 16, 64);
-      if (g4 >= 1) x += y;
-      y = __shfl_up(x, 32, 64);
-      if (g4 >= 2) x += y;
-      const float excl = x - tot;  // sum of earlier token groups of this sub-chunk
+      const float excl = rows_exclusive_sum(lam[3][i], g4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) lam[r][i] += excl;  // now relative to the sub-chunk start
-      rloc[i] = __shfl(lam[3][i], 16 + co, 64);       // token 7 of the sub-chunk
-      if (g4 == 3) sm.wtot[wave][ch0 + i] = lam[3][i];
-      if (g4 == 1) sm.rloc[wave][ch0 + i] = lam[3][i];
+      for (int r = 0; r < 4; ++r) lam[r][i] += excl;
+    }
+    if (g4 == 1) {
+      *reinterpret_cast<f32x4*>(&sm.rloc[wave][ch0]) = f32x4{lam[3][0], lam[3][1], lam[3][2], lam[3][3]};
+      *reinterpret_cast<f32x4*>(&sm.rloc[wave][ch0 + 4]) = f32x4{lam[3][4], lam[3][5], lam[3][6], lam[3][7]};
+    }
+    if (g4 == 3) {
+      *reinterpret_cast<f32x4*>(&sm.wtot[wave][ch0]) = f32x4{lam[3][0], lam[3][1], lam[3][2], lam[3][3]};
+      *reinterpret_cast<f32x4*>(&sm.wtot[wave][ch0 + 4]) = f32x4{lam[3][4], lam[3][5], lam[3][6], lam[3][7]};
     }
     __syncthreads();
 
-    // chunk-relative references and totals
-    float R[8], GL[8], Rw[8];
+    // ---------------- decay factors and MFMA operands ----------------
+    // R: G at token 7 of this sub-chunk (relative to the sub-chunk start);
+    // pre: G before the sub-chunk; tot: G at the chunk's last token
+    float eR[8];
+    {
+      float R[8], eLR[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float pre = 0.f, all = 0.f;
+      for (int i = 0; i < 8; ++i) {
+        R[i] = sm.rloc[wave][ch0 + i];
+        float pre = 0.f, tot = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float wt = sm.wtot[w][ch0 + i];
-        if (w < wave) pre += wt;
-        all += wt;
+        for (int w = 0; w < 4; ++w) {
+          const float wt = sm.wtot[w][ch0 + i];
+          if (w < wave) pre += wt;
+          tot += wt;
+        }
+        eR[i] = ex2(pre + R[i]);          // e^{R} from the chunk start
+        eLR[i] = ex2(tot - pre - R[i]);   // e^{G_last - R}
       }
-      Rw[i] = pre;             // G just before this sub-chunk
-      R[i] = pre + rloc[i];    // reference: G at token 7 of this sub-chunk
-      GL[i] = all;             // G at the last token of the chunk
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * tq + r;
+        float ke[8], qe[8], kfv[8], kph[8], kpl[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float E = ex2(lam[r][i] - R[i]);
+          const float F = ex2(R[i] - lam[r][i]);
+          kfv[i] = kf[r][i] * F;
+          ke[i] = kf[r][i] * E;
+          qe[i] = qf[r][i] * E;
+          const float kp = kfv[i] * eLR[i];  // e^{G_last - G_t} k^
+          const float hi = (float)(bf16)kp;
+          kph[i] = hi;
+          kpl[i] = kp - hi;
+        }
+        *reinterpret_cast<bf16x8*>(&sm.ke[t][ch0]) = pack8(ke);
+        *reinterpret_cast<bf16x8*>(&sm.qe[t][ch0]) = pack8(qe);
+        *reinterpret_cast<bf16x8*>(&sm.r2.kf[t][ch0]) = pack8(kfv);
+        *reinterpret_cast<bf16x8*>(&sm.kph[t][ch0]) = pack8(kph);
+        *reinterpret_cast<bf16x8*>(&sm.kpl[t][ch0]) = pack8(kpl);
+      }
     }
-    // per-channel tables shared by all waves
     for (int idx = tid; idx < 6 * 128; idx += kThreads) {
       const int pr = idx >> 7, c = idx & 127;
       const int a = pr < 1 ? 1 : pr < 3 ? 2 : 3;
@@ -316,52 +420,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
       for (int w = bb; w < a; ++w) d += sm.wtot[w][c];
       sm.dab[pr][c] = ex2(d);
     }
-    if (tid < 16) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sm.gam[ch0 + i] = ex2(GL[i]);
-    }
-
-    // operands
-    float eR[8], eLR[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      eR[i] = ex2(R[i]);           // e^{R}, relative to the chunk start
-      eLR[i] = ex2(GL[i] - R[i]);  // e^{G_last - R}
-    }
-    float xw[4][8], kph[4][8], kpl[4][8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 4 * tq + r;
-      float ke[8], qe[8], kfv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float Gt = lam[r][i] + Rw[i];  // chunk-relative G
-        const float E = ex2(Gt - R[i]);
-        const float F = ex2(R[i] - Gt);
-        ke[i] = kf[r][i] * E;
-        qe[i] = qf[r][i] * E;
-        kfv[i] = kf[r][i] * F;
-        const float kp = kfv[i] * eLR[i];  // e^{G_last - G_t} k^
-        const float hi = (float)(bf16)kp;
-        kph[r][i] = hi;
-        kpl[r][i] = kp - hi;
-      }
-      const bf16x8 keb = pack8(ke);
-      *reinterpret_cast<bf16x8*>(&sm.r0.ke[t][ch0]) = keb;
-      *reinterpret_cast<bf16x8*>(&sm.qe[t][ch0]) = pack8(qe);
-      *reinterpret_cast<bf16x8*>(&sm.kf[t][ch0]) = pack8(kfv);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xw[r][i] = (float)keb[i] * eR[i];  // e^G k^ from the bf16 k^ e^{G-R}
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<bf16x4*>(&sm.xwt[ch0 + i][4 * tq]) =
-          bf16x4{(bf16)xw[0][i], (bf16)xw[1][i], (bf16)xw[2][i], (bf16)xw[3][i]};
-      *reinterpret_cast<bf16x4*>(&sm.kph[ch0 + i][4 * tq]) =
-          bf16x4{(bf16)kph[0][i], (bf16)kph[1][i], (bf16)kph[2][i], (bf16)kph[3][i]};
-      *reinterpret_cast<bf16x4*>(&sm.kpl[ch0 + i][4 * tq]) =
-          bf16x4{(bf16)kpl[0][i], (bf16)kpl[1][i], (bf16)kpl[2][i], (bf16)kpl[3][i]};
-    }
+    if (tid < 128) sm.gam[tid] = ex2(sm.wtot[0][tid] + sm.wtot[1][tid] + sm.wtot[2][tid] + sm.wtot[3][tid]);
     __syncthreads();
 
     // ---------------- A and Mq blocks (bf16 MFMA over the 128 channels) ----------------
@@ -371,124 +430,148 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
       const int pi = wave + 4 * k3;
       Mreg[k3] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (pi >= 10) continue;
-      const int a = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
-      const int bb = pi - (a * (a + 1)) / 2;
+      int a, bb;
+      pair_ab(pi, a, bb);
       f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int c0 = 32 * ks + 8 * g4;
-        const bf16x8 aK = *reinterpret_cast<const bf16x8*>(&sm.r0.ke[16 * a + l16][c0]);
+        const bf16x8 aK = *reinterpret_cast<const bf16x8*>(&sm.ke[16 * a + l16][c0]);
         const bf16x8 aQ = *reinterpret_cast<const bf16x8*>(&sm.qe[16 * a + l16][c0]);
-        bf16x8 bK = *reinterpret_cast<const bf16x8*>(&sm.kf[16 * bb + l16][c0]);
+        bf16x8 bK = *reinterpret_cast<const bf16x8*>(&sm.r2.kf[16 * bb + l16][c0]);
         if (bb < a) {
-          const float* d = &sm.dab[(a * (a - 1)) / 2 + bb][c0];
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.dab[(a * (a - 1)) / 2 + bb][c0]);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.dab[(a * (a - 1)) / 2 + bb][c0 + 4]);
           float f[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) f[i] = (float)bK[i] * d[i];
+          for (int i = 0; i < 4; ++i) {
+            f[i] = (float)bK[i] * d0[i];
+            f[4 + i] = (float)bK[4 + i] * d1[i];
+          }
           bK = pack8(f);
         }
         accA = mfma32(aK, bK, accA);
         accM = mfma32(aQ, bK, accM);
       }
+      f32x4 at;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * g4 + j;  // row inside the block
         const bool keepA = bb < a || l16 < r;
         const bool keepM = bb < a || l16 <= r;
         const float av = keepA ? accA[j] * sm.beta[16 * a + r] : 0.f;
-        if (bb == a) sm.adiag[a][r][l16] = av;
-        else sm.aoff[16 * a + r][16 * bb + l16] = (bf16)av;
+        at[j] = av;
+        if (bb < a) sm.aoff[16 * a + r][16 * bb + l16] = (bf16)av;
         Mreg[k3][j] = keepM ? accM[j] : 0.f;
       }
+      if (bb == a) *reinterpret_cast<f32x4*>(&sm.adt[a][l16][4 * g4]) = at;
     }
     __syncthreads();
 
-    // ---------------- Tm = (I + A)^-1: diagonal blocks by forward substitution ----------------
+    // ---------------- (I + A)^-1 on the diagonal blocks; q, k operands -> e^G ----------------
     if (lane < 16) {
       const int a = wave, c = lane;
       float x[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = (r == c) ? 1.f : 0.f;
+      for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+      // pivot-outer forward substitution: the dependent chain is 15 steps long
 #pragma unroll
-        for (int m = 0; m < r; ++m) acc = fmaf(-sm.adiag[a][r][m], x[m], acc);
-        x[r] = acc;
+      for (int m = 0; m < 15; ++m) {
+        float col[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v4 = *reinterpret_cast<const f32x4*>(&sm.adt[a][m][4 * q4]);
+          col[4 * q4] = v4[0]; col[4 * q4 + 1] = v4[1]; col[4 * q4 + 2] = v4[2]; col[4 * q4 + 3] = v4[3];
+        }
+#pragma unroll
+        for (int r = m + 1; r < 16; ++r) x[r] = fmaf(-col[r], x[m], x[r]);
       }
-      const int bi = blk(a, a);
       const float bc = sm.beta[16 * a + c];
+      bf16x8 c0v, c1v;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        sm.r0.tb.row[bi][r][c] = (bf16)x[r];
-        sm.r0.tb.col[bi][c][r] = (bf16)x[r];
+        const bf16 xb = (bf16)x[r];
+        sm.r2.d.row[a][r][c] = xb;
+        if (r < 8) c0v[r] = xb; else c1v[r - 8] = xb;
         sm.lb[16 * a + r][16 * a + c] = (bf16)((x[r] - (r == c ? 1.f : 0.f)) * bc);
+      }
+      *reinterpret_cast<bf16x8*>(&sm.r2.d.col[a][c][0]) = c0v;
+      *reinterpret_cast<bf16x8*>(&sm.r2.d.col[a][c][8]) = c1v;
+    }
+    // e^G k^ (W's right operand) and e^G (scale q^) (O's left operand), in place
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * tq + r;
+      const bf16x8 k8 = *reinterpret_cast<const bf16x8*>(&sm.ke[t][ch0]);
+      const bf16x8 q8 = *reinterpret_cast<const bf16x8*>(&sm.qe[t][ch0]);
+      float fk[8], fq[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        fk[i] = (float)k8[i] * eR[i];
+        fq[i] = (float)q8[i] * eR[i];
+      }
+      *reinterpret_cast<bf16x8*>(&sm.ke[t][ch0]) = pack8(fk);
+      *reinterpret_cast<bf16x8*>(&sm.qe[t][ch0]) = pack8(fq);
+    }
+    __syncthreads();
+
+    // ---------------- off-diagonal blocks: wave b builds column b of Tm ----------------
+    // T_ab = -D_a sum_{c=b}^{a-1} A_ac T_cb, with T_bb = D_b
+    if (wave < 3) {
+      const int bb = wave;
+      bf16x4 Tc[4];  // T_cb of this column as B operands (c > b)
+#pragma unroll
+      for (int a = 1; a < 4; ++a) {
+        if (a <= bb) continue;
+        f32x4 X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (c < bb || c >= a) continue;
+          const bf16x4 Aop = *reinterpret_cast<const bf16x4*>(&sm.aoff[16 * a + l16][16 * c + 4 * g4]);
+          const bf16x4 Bop = c == bb ? *reinterpret_cast<const bf16x4*>(&sm.r2.d.col[bb][l16][4 * g4]) : Tc[c];
+          X = mfma16(Aop, Bop, X);
+        }
+        const bf16x4 Dop = *reinterpret_cast<const bf16x4*>(&sm.r2.d.row[a][l16][4 * g4]);
+        const f32x4 Tv = mfma16(Dop, to_bf16x4(X), f32x4{0.f, 0.f, 0.f, 0.f});
+        const float bc = sm.beta[16 * bb + l16];
+        f32x4 Tn;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          Tn[j] = -Tv[j];
+          sm.lb[16 * a + 4 * g4 + j][16 * bb + l16] = (bf16)(Tn[j] * bc);
+        }
+        Tc[a] = to_bf16x4(Tn);
       }
     }
     __syncthreads();
 
-    // ---------------- off-diagonal blocks: T_ab = -D_a sum_c A_ac T_cb ----------------
-#pragma unroll
-    for (int lev = 1; lev < 4; ++lev) {
-      if (wave < 4 - lev) {
-        const int a = wave + lev, bb = wave;
-        f32x4 X = {0.f, 0.f, 0.f, 0.f};
-        for (int c = bb; c < a; ++c) {
-          const bf16x4 Aop = *reinterpret_cast<const bf16x4*>(&sm.aoff[16 * a + l16][16 * c + 4 * g4]);
-          const bf16x4 Bop = *reinterpret_cast<const bf16x4*>(&sm.r0.tb.col[blk(c, bb)][l16][4 * g4]);
-          X = mfma16(Aop, Bop, X);
-        }
-        const bf16x4 Dop = *reinterpret_cast<const bf16x4*>(&sm.r0.tb.row[blk(a, a)][l16][4 * g4]);
-        f32x4 Tv = mfma16(Dop, to_bf16x4(X), f32x4{0.f, 0.f, 0.f, 0.f});
-        const int bi = blk(a, bb);
-        const float bc = sm.beta[16 * bb + l16];
-        bf16x4 tcol;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float t = -Tv[j];
-          tcol[j] = (bf16)t;
-          sm.r0.tb.row[bi][4 * g4 + j][l16] = (bf16)t;
-          sm.lb[16 * a + 4 * g4 + j][16 * bb + l16] = (bf16)(t * bc);
-        }
-        *reinterpret_cast<bf16x4*>(&sm.r0.tb.col[bi][l16][4 * g4]) = tcol;
-      }
-      __syncthreads();
-    }
-
-    // ---------------- Mq into the free A buffer; q operand -> e^G q; W ----------------
+    // ---------------- Mq into the free A buffer; W = b X + L X with X = e^G k^ ----------------
 #pragma unroll
     for (int k3 = 0; k3 < 3; ++k3) {
       const int pi = wave + 4 * k3;
       if (pi >= 10) continue;
-      const int a = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
-      const int bb = pi - (a * (a + 1)) / 2;
+      int a, bb;
+      pair_ab(pi, a, bb);
 #pragma unroll
       for (int j = 0; j < 4; ++j) sm.aoff[16 * a + 4 * g4 + j][16 * bb + l16] = (bf16)Mreg[k3][j];
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 4 * tq + r;
-      const bf16x8 q8 = *reinterpret_cast<const bf16x8*>(&sm.qe[t][ch0]);
-      float f[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = (float)q8[i] * eR[i];
-      *reinterpret_cast<bf16x8*>(&sm.qe[t][ch0]) = pack8(f);
     }
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       const int ct = wave + 4 * k2;  // 16-channel column tile of W
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const bf16x4 x4 = *reinterpret_cast<const bf16x4*>(&sm.xwt[16 * ct + l16][16 * a + 4 * g4]);
-        f32x4 acc;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = sm.beta[16 * a + 4 * g4 + j] * (float)x4[j];
+        const bf16x4 x4 = rows4(sm.ke, 16 * a + 4 * g4, 16 * ct, l16);
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[16 * a + 4 * g4]);
+        f32x4 acc = bt * to_f32x4(x4);
 #pragma unroll
         for (int ks = 0; ks < (a >= 2 ? 2 : 1); ++ks) {
           const bf16x8 Aop = *reinterpret_cast<const bf16x8*>(&sm.lb[16 * a + l16][32 * ks + 8 * g4]);
-          const bf16x8 Bop = *reinterpret_cast<const bf16x8*>(&sm.xwt[16 * ct + l16][32 * ks + 8 * g4]);
+          const bf16x8 Bop = cat(rows4(sm.ke, 32 * ks + 8 * g4, 16 * ct, l16),
+                                 rows4(sm.ke, 32 * ks + 8 * g4 + 4, 16 * ct, l16));
           acc = mfma32(Aop, Bop, acc);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sm.r0.wn[16 * a + 4 * g4 + j][16 * ct + l16] = (bf16)(-acc[j]);
+        for (int j = 0; j < 4; ++j) sm.r2.wn[16 * a + 4 * g4 + j][16 * ct + l16] = (bf16)(-acc[j]);
       }
     }
     __syncthreads();
@@ -498,8 +581,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
     for (int st = 0; st < SPW; ++st) {
       const int s = wave + 4 * st;
       if (s >= NS) break;
-      const int jl = 16 * s + l16;
-      const int jg = slice * VS + jl;
+      const int jl = 16 * s;
       bf16x8 Sb[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) Sb[kb] = cat(to_bf16x4(S[st][2 * kb]), to_bf16x4(S[st][2 * kb + 1]));
@@ -508,17 +590,17 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
       f32x4 N[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const bf16x4 v4 = *reinterpret_cast<const bf16x4*>(&sm.vt[jl][16 * rt + 4 * g4]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) N[rt][j] = sm.beta[16 * rt + 4 * g4 + j] * (float)v4[j];
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[16 * rt + 4 * g4]);
+        N[rt] = bt * to_f32x4(rows4(sm.v, 16 * rt + 4 * g4, jl, l16));
 #pragma unroll
         for (int ks = 0; ks < (rt >= 2 ? 2 : 1); ++ks) {
           const bf16x8 Aop = *reinterpret_cast<const bf16x8*>(&sm.lb[16 * rt + l16][32 * ks + 8 * g4]);
-          const bf16x8 Bop = *reinterpret_cast<const bf16x8*>(&sm.vt[jl][32 * ks + 8 * g4]);
+          const bf16x8 Bop = cat(rows4(sm.v, 32 * ks + 8 * g4, jl, l16),
+                                 rows4(sm.v, 32 * ks + 8 * g4 + 4, jl, l16));
           N[rt] = mfma32(Aop, Bop, N[rt]);
         }
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) N[rt] = mfma32(perm_row(sm.r0.wn, 16 * rt + l16, 32 * kb, g4), Sb[kb], N[rt]);
+        for (int kb = 0; kb < 4; ++kb) N[rt] = mfma32(perm_row(sm.r2.wn, 16 * rt + l16, 32 * kb, g4), Sb[kb], N[rt]);
       }
 
       // O = (e^G q) S + Mq N
@@ -541,10 +623,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
 #pragma unroll
         for (int kb = 0; kb < (rt >= 2 ? 2 : 1); ++kb)
           O[rt] = mfma32(perm_row(sm.aoff, 16 * rt + l16, 32 * kb, g4), Nh[kb], O[rt]);
+        const bf16x4 ob = to_bf16x4(O[rt]);
+        bf16* orow = reinterpret_cast<bf16*>(outb) + jl + l16;
+        if (L == kC) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t = 16 * rt + 4 * g4 + j;
-          if (t < L) p.out[((size_t)(t0 + t) * H + h) * kD + jg] = f32_to_bf16(O[rt][j]);
+          for (int j = 0; j < 4; ++j)
+            orow[(unsigned)(t0 + 16 * rt + 4 * g4 + j) * (unsigned)rowstride] = ob[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int t = 16 * rt + 4 * g4 + j;
+            if (t < L) orow[(unsigned)(t0 + t) * (unsigned)rowstride] = ob[j];
+          }
         }
       }
 
@@ -555,8 +645,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
         S[st][rt] *= gm;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 Ah = perm_row(sm.kph, 16 * rt + l16, 32 * kb, g4);
-          const bf16x8 Al = perm_row(sm.kpl, 16 * rt + l16, 32 * kb, g4);
+          const bf16x8 Ah = cat(rows4(sm.kph, 32 * kb + 4 * g4, 16 * rt, l16),
+                                rows4(sm.kph, 32 * kb + 16 + 4 * g4, 16 * rt, l16));
+          const bf16x8 Al = cat(rows4(sm.kpl, 32 * kb + 4 * g4, 16 * rt, l16),
+                                rows4(sm.kpl, 32 * kb + 16 + 4 * g4, 16 * rt, l16));
           S[st][rt] = mfma32(Ah, Nh[kb], S[st][rt]);
           S[st][rt] = mfma32(Ah, Nl[kb], S[st][rt]);
           S[st][rt] = mfma32(Al, Nh[kb], S[st][rt]);
@@ -576,7 +668,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const size_t idx = sbase + (size_t)(16 * rt + 4 * g4 + j) * kD + jg;
-        if (p.state_bf16) static_cast<uint16_t*>(p.sT)[idx] = f32_to_bf16(S[st][rt][j]);
+        if (p.state_bf16) static_cast<bf16*>(p.sT)[idx] = (bf16)S[st][rt][j];
         else static_cast<float*>(p.sT)[idx] = S[st][rt][j];
       }
   }

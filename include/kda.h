@@ -86,7 +86,9 @@ size_t kda_get_workspace_size(int64_t max_tokens, int32_t heads, int32_t max_seq
  *   stream         hipStream_t to queue the work on (NULL = default stream)
  *
  * q, k, v, g, beta_logits and out may be NULL when num_tokens is 0; every other
- * pointer except initial_state and workspace is required.
+ * pointer except initial_state and workspace is required.  Size limits:
+ * num_tokens * heads * 128 < 2^31 (token rows are addressed with 32-bit
+ * element offsets), heads <= 65536, num_seqs * heads * 8 < 2^31.
  *
  * Work is queued on the stream and the call returns without waiting: no host
  * synchronisation, no allocation and no device-to-host copy, so the call can be

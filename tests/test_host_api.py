@@ -98,6 +98,7 @@ def test_null_required_pointer_rejected(name):
     dict(T=-1), dict(T=2 ** 31), dict(H=0), dict(H=-3), dict(N=0), dict(N=-1),
     dict(sdt=2), dict(sdt=-1), dict(lb=float("nan")), dict(lb=float("-inf")),
     dict(scale=float("inf")), dict(scale=float("nan")), dict(N=2 ** 28, H=16),
+    dict(T=2 ** 20, H=16), dict(T=2 ** 24, H=1),
 ])
 def test_bad_sizes_and_scalars_rejected(over):
     assert _call(**over) == INVALID
