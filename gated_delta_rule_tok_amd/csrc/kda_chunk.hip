@@ -183,7 +183,7 @@ struct Prefetch {
   static constexpr int VN = VS / 16;
   uint4 q[4], k[4], g[4];
   bf16 v[4][VN];
-  float beta;
+  uint16_t beta;  // raw bits: converting here would wait for the load
 };
 
 template <int VS>
@@ -204,19 +204,20 @@ __device__ __forceinline__ void load_row(Prefetch<VS>& pf, int r, const uint16_t
   }
 }
 
-// Fetch chunk [t0, t0 + L).  Offsets are 32-bit from per-call base pointers
-// (q/k/g/v already point at this thread's channels of token 0, head h).
+// Fetch chunk [t0, t0 + L).  Offsets are 32-bit from uniform base pointers
+// (q/k/g/v point at token 0 of head h; v at this slice's first column).
 template <int VS>
 __device__ __forceinline__ void load_chunk(Prefetch<VS>& pf, const uint16_t* q, const uint16_t* k,
                                            const uint16_t* g, const uint16_t* v,
                                            const uint16_t* beta, int rowstride, int H, int t0,
                                            int L, int tq, int tid) {
   constexpr int VN = Prefetch<VS>::VN;
+  const unsigned ck = 8u * (unsigned)(tid & 15), cv = (unsigned)(tid & 15) * VN;
   if (L == kC) {  // full chunk: no per-row predicates
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const unsigned off = (unsigned)(t0 + 4 * tq + r) * (unsigned)rowstride;
-      load_row<VS>(pf, r, q + off, k + off, g + off, v + off);
+      load_row<VS>(pf, r, q + (off + ck), k + (off + ck), g + (off + ck), v + (off + cv));
     }
   } else {
 #pragma unroll
@@ -224,7 +225,7 @@ __device__ __forceinline__ void load_chunk(Prefetch<VS>& pf, const uint16_t* q, 
       const int t = 4 * tq + r;
       if (t < L) {
         const unsigned off = (unsigned)(t0 + t) * (unsigned)rowstride;
-        load_row<VS>(pf, r, q + off, k + off, g + off, v + off);
+        load_row<VS>(pf, r, q + (off + ck), k + (off + ck), g + (off + ck), v + (off + cv));
       } else {
         pf.q[r] = pf.k[r] = pf.g[r] = uint4{0, 0, 0, 0};
 #pragma unroll
@@ -232,7 +233,75 @@ __device__ __forceinline__ void load_chunk(Prefetch<VS>& pf, const uint16_t* q, 
       }
     }
   }
-  pf.beta = (tid < L) ? bf16_to_f32(beta[(unsigned)(t0 + tid) * (unsigned)H]) : 0.f;
+  pf.beta = (tid < L) ? beta[(unsigned)(t0 + tid) * (unsigned)H] : uint16_t(0);
+}
+
+// Elementwise pass of one chunk, kept in registers until the chunk's operand
+// phase: raw q and k, their per-token inverse norms (q's includes scale), the
+// log2 decay summed from the start of this wave's 16-token sub-chunk, and the
+// raw value slice and beta logit.  Writes the sub-chunk's reference value
+// (token 7) and total to LDS for the operand phase.
+template <int VS>
+struct Elem {
+  uint4 q[4], k[4];
+  float rq[4], rk[4];
+  float lam[4][8];
+  bf16 v[4][Prefetch<VS>::VN];
+  float beta;
+};
+
+template <int VS>
+__device__ __forceinline__ void elementwise(Elem<VS>& el, const Prefetch<VS>& pf, int L, int tq,
+                                            int g4, const float* c2, float c1, float lb2,
+                                            float scale, float* rloc_row, float* wtot_row) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float qf[8], kf[8], gf[8];
+    unpack8(pf.q[r], qf);
+    unpack8(pf.k[r], kf);
+    unpack8(pf.g[r], gf);
+    el.q[r] = pf.q[r];
+    el.k[r] = pf.k[r];
+#pragma unroll
+    for (int c = 0; c < Prefetch<VS>::VN; ++c) el.v[r][c] = pf.v[r][c];
+    float qq = 0.f, kk = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      qq = fmaf(qf[i], qf[i], qq);
+      kk = fmaf(kf[i], kf[i], kk);
+    }
+    el.rq[r] = rsqrtf(row_sum16(qq) + kNormEps) * scale;
+    el.rk[r] = rsqrtf(row_sum16(kk) + kNormEps);
+    const bool valid = 4 * tq + r < L;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // log2 of the decay: lb * sigmoid(exp(A_log) (g + dt_bias)) * log2(e)
+      const float e = ex2(fmaf(gf[i], c1, c2[i]));
+      el.lam[r][i] = valid ? lb2 * rcp(1.f + e) : 0.f;
+    }
+  }
+  el.beta = bf16_to_f32(pf.beta);
+  // inclusive cumulative sum from the start of this wave's 16-token sub-chunk
+#pragma unroll
+  for (int r = 1; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) el.lam[r][i] += el.lam[r - 1][i];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float excl = rows_exclusive_sum(el.lam[3][i], g4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) el.lam[r][i] += excl;
+  }
+  const f32x4 lo = f32x4{el.lam[3][0], el.lam[3][1], el.lam[3][2], el.lam[3][3]};
+  const f32x4 hi = f32x4{el.lam[3][4], el.lam[3][5], el.lam[3][6], el.lam[3][7]};
+  if (g4 == 1) {  // token 7 of the sub-chunk
+    reinterpret_cast<f32x4*>(rloc_row)[0] = lo;
+    reinterpret_cast<f32x4*>(rloc_row)[1] = hi;
+  }
+  if (g4 == 3) {  // sub-chunk total
+    reinterpret_cast<f32x4*>(wtot_row)[0] = lo;
+    reinterpret_cast<f32x4*>(wtot_row)[1] = hi;
+  }
 }
 
 template <int VS>
@@ -299,76 +368,28 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
   // base pointers of token 0 for this head (and this thread's channels);
   // per-token offsets below are 32-bit (T * H * 128 < 2^31 elements is checked on the host)
   const int rowstride = H * kD;
-  const uint16_t* qb = p.q + (size_t)h * kD + 8 * co;
-  const uint16_t* kb = p.k + (size_t)h * kD + 8 * co;
-  const uint16_t* gb = p.g + (size_t)h * kD + 8 * co;
-  const uint16_t* vb = p.v + (size_t)h * kD + slice * VS + co * VN;
+  const uint16_t* qb = p.q + (size_t)h * kD;
+  const uint16_t* kb = p.k + (size_t)h * kD;
+  const uint16_t* gb = p.g + (size_t)h * kD;
+  const uint16_t* vb = p.v + (size_t)h * kD + slice * VS;
   const uint16_t* betab = p.beta + h;
   uint16_t* outb = p.out + (size_t)h * kD + slice * VS;
 
   Prefetch<VS> pf;
-  if (bos < eos) load_chunk<VS>(pf, qb, kb, gb, vb, betab, rowstride, H, bos, min(kC, eos - bos), tq, tid);
+  Elem<VS> el;
+  if (bos < eos) {
+    load_chunk<VS>(pf, qb, kb, gb, vb, betab, rowstride, H, bos, min(kC, eos - bos), tq, tid);
+    elementwise<VS>(el, pf, min(kC, eos - bos), tq, g4, c2, c1, lb2, p.scale, &sm.rloc[wave][ch0],
+                    &sm.wtot[wave][ch0]);
+  }
 
   for (int t0 = bos; t0 < eos; t0 += kC) {
     const int L = min(kC, eos - t0);
     __syncthreads();  // the previous chunk is done with every shared buffer
 
-    // ---------------- elementwise: norms, gate, cumulative decay ----------------
-    float qf[4][8], kf[4][8], lam[4][8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      unpack8(pf.q[r], qf[r]);
-      unpack8(pf.k[r], kf[r]);
-      unpack8(pf.g[r], lam[r]);
-#pragma unroll
-      for (int c = 0; c < VN; ++c) sm.v[4 * tq + r][co * VN + c] = pf.v[r][c];
-    }
-    if (tid < kC) sm.beta[tid] = tid < L ? rcp(1.f + ex2(-kLog2e * pf.beta)) : 0.f;
-
-    // the registers are free again: fetch the next chunk behind this one's compute
-    if (t0 + kC < eos)
-      load_chunk<VS>(pf, qb, kb, gb, vb, betab, rowstride, H, t0 + kC, min(kC, eos - t0 - kC), tq, tid);
-
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float qq = 0.f, kk = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        qq = fmaf(qf[r][i], qf[r][i], qq);
-        kk = fmaf(kf[r][i], kf[r][i], kk);
-      }
-      const float rq = rsqrtf(row_sum16(qq) + kNormEps) * p.scale;
-      const float rk = rsqrtf(row_sum16(kk) + kNormEps);
-      const bool valid = 4 * tq + r < L;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        qf[r][i] *= rq;
-        kf[r][i] *= rk;
-        // log2 of the decay: lb * sigmoid(exp(A_log) (g + dt_bias)) * log2(e)
-        const float e = ex2(fmaf(lam[r][i], c1, c2[i]));
-        lam[r][i] = valid ? lb2 * rcp(1.f + e) : 0.f;
-      }
-    }
-    // inclusive cumulative sum from the start of this wave's 16-token sub-chunk
-#pragma unroll
-    for (int r = 1; r < 4; ++r)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) lam[r][i] += lam[r - 1][i];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float excl = rows_exclusive_sum(lam[3][i], g4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) lam[r][i] += excl;
-    }
-    if (g4 == 1) {
-      *reinterpret_cast<f32x4*>(&sm.rloc[wave][ch0]) = f32x4{lam[3][0], lam[3][1], lam[3][2], lam[3][3]};
-      *reinterpret_cast<f32x4*>(&sm.rloc[wave][ch0 + 4]) = f32x4{lam[3][4], lam[3][5], lam[3][6], lam[3][7]};
-    }
-    if (g4 == 3) {
-      *reinterpret_cast<f32x4*>(&sm.wtot[wave][ch0]) = f32x4{lam[3][0], lam[3][1], lam[3][2], lam[3][3]};
-      *reinterpret_cast<f32x4*>(&sm.wtot[wave][ch0 + 4]) = f32x4{lam[3][4], lam[3][5], lam[3][6], lam[3][7]};
-    }
-    __syncthreads();
+    // fetch the next chunk; its elementwise pass runs during this chunk's state part
+    const int Ln = min(kC, eos - t0 - kC);  // <= 0 when this is the last chunk
+    if (Ln > 0) load_chunk<VS>(pf, qb, kb, gb, vb, betab, rowstride, H, t0 + kC, Ln, tq, tid);
 
     // ---------------- decay factors and MFMA operands ----------------
     // R: G at token 7 of this sub-chunk (relative to the sub-chunk start);
@@ -392,14 +413,19 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * tq + r;
-        float ke[8], qe[8], kfv[8], kph[8], kpl[8];
+        float qf[8], kf[8], ke[8], qe[8], kfv[8], kph[8], kpl[8];
+        unpack8(el.q[r], qf);
+        unpack8(el.k[r], kf);
+#pragma unroll
+        for (int c = 0; c < VN; ++c) sm.v[t][co * VN + c] = el.v[r][c];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float E = ex2(lam[r][i] - R[i]);
-          const float F = ex2(R[i] - lam[r][i]);
-          kfv[i] = kf[r][i] * F;
-          ke[i] = kf[r][i] * E;
-          qe[i] = qf[r][i] * E;
+          const float E = ex2(el.lam[r][i] - R[i]);
+          const float F = ex2(R[i] - el.lam[r][i]);
+          const float kn = kf[i] * el.rk[r];
+          kfv[i] = kn * F;
+          ke[i] = kn * E;
+          qe[i] = qf[i] * el.rq[r] * E;
           const float kp = kfv[i] * eLR[i];  // e^{G_last - G_t} k^
           const float hi = (float)(bf16)kp;
           kph[i] = hi;
@@ -412,6 +438,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
         *reinterpret_cast<bf16x8*>(&sm.kpl[t][ch0]) = pack8(kpl);
       }
     }
+    if (tid < kC) sm.beta[tid] = tid < L ? rcp(1.f + ex2(-kLog2e * el.beta)) : 0.f;
     for (int idx = tid; idx < 6 * 128; idx += kThreads) {
       const int pr = idx >> 7, c = idx & 127;
       const int a = pr < 1 ? 1 : pr < 3 ? 2 : 3;
@@ -469,34 +496,44 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
     __syncthreads();
 
     // ---------------- (I + A)^-1 on the diagonal blocks; q, k operands -> e^G ----------------
-    if (lane < 16) {
-      const int a = wave, c = lane;
-      float x[16];
+    {
+      // D = (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) for the strictly lower
+      // 16x16 block N = A_aa (N^16 = 0), one block per wave.  Every product is
+      // formed together with its transpose: an accumulator holds Z[4g+j][l16],
+      // which is Z's B-operand layout and Z^T's A-operand layout, so Z = X Y is
+      // mfma(X^T, Y) and Z^T = Y^T X^T is mfma(Y, X^T).
+      const int a = wave;
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 Nn = *reinterpret_cast<const f32x4*>(&sm.adt[a][l16][4 * g4]);  // N[4g+j][l16]
+      f32x4 Nt;                                                                  // N[l16][4g+j]
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
-      // pivot-outer forward substitution: the dependent chain is 15 steps long
+      for (int j = 0; j < 4; ++j) Nt[j] = sm.adt[a][4 * g4 + j][l16];
+      f32x4 I4;
 #pragma unroll
-      for (int m = 0; m < 15; ++m) {
-        float col[16];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 v4 = *reinterpret_cast<const f32x4*>(&sm.adt[a][m][4 * q4]);
-          col[4 * q4] = v4[0]; col[4 * q4 + 1] = v4[1]; col[4 * q4 + 2] = v4[2]; col[4 * q4 + 3] = v4[3];
-        }
-#pragma unroll
-        for (int r = m + 1; r < 16; ++r) x[r] = fmaf(-col[r], x[m], x[r]);
-      }
-      const float bc = sm.beta[16 * a + c];
-      bf16x8 c0v, c1v;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bf16 xb = (bf16)x[r];
-        sm.r2.d.row[a][r][c] = xb;
-        if (r < 8) c0v[r] = xb; else c1v[r - 8] = xb;
-        sm.lb[16 * a + r][16 * a + c] = (bf16)((x[r] - (r == c ? 1.f : 0.f)) * bc);
-      }
-      *reinterpret_cast<bf16x8*>(&sm.r2.d.col[a][c][0]) = c0v;
-      *reinterpret_cast<bf16x8*>(&sm.r2.d.col[a][c][8]) = c1v;
+      for (int j = 0; j < 4; ++j) I4[j] = (4 * g4 + j == l16) ? 1.f : 0.f;
+      const bf16x4 nb = to_bf16x4(Nn), ntb = to_bf16x4(Nt);
+      const f32x4 N2 = mfma16(ntb, nb, zero), N2t = mfma16(nb, ntb, zero);
+      const bf16x4 n2b = to_bf16x4(N2), n2tb = to_bf16x4(N2t);
+      const f32x4 N4 = mfma16(n2tb, n2b, zero), N4t = mfma16(n2b, n2tb, zero);
+      const bf16x4 n4b = to_bf16x4(N4), n4tb = to_bf16x4(N4t);
+      const f32x4 N8 = mfma16(n4tb, n4b, zero);
+      // P1 = I - N + N^2 - N N^2
+      const f32x4 P1 = mfma16(ntb, to_bf16x4(-N2), I4 - Nn + N2);
+      const f32x4 P1t = mfma16(n2b, to_bf16x4(-Nt), I4 - Nt + N2t);
+      // P2 = P1 (I + N^4)
+      const bf16x4 p1tb = to_bf16x4(P1t);
+      const f32x4 P2 = mfma16(p1tb, n4b, P1);
+      const f32x4 P2t = mfma16(n4b, p1tb, P1t);
+      // D = P2 (I + N^8)
+      const bf16x4 p2tb = to_bf16x4(P2t), n8b = to_bf16x4(N8);
+      const f32x4 D = mfma16(p2tb, n8b, P2);    // D[4g+j][l16]
+      const f32x4 Dt = mfma16(n8b, p2tb, P2t);  // D[l16][4g+j]
+      // row-major D (A operand of D_a X), column-major D (B operand of A_ab D_b),
+      // and the diagonal block of L = (D - I) diag(b)
+      *reinterpret_cast<bf16x4*>(&sm.r2.d.row[a][l16][4 * g4]) = to_bf16x4(Dt);
+      *reinterpret_cast<bf16x4*>(&sm.r2.d.col[a][l16][4 * g4]) = to_bf16x4(D);
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[16 * a + 4 * g4]);
+      *reinterpret_cast<bf16x4*>(&sm.lb[16 * a + l16][16 * a + 4 * g4]) = to_bf16x4((Dt - I4) * bt);
     }
     // e^G k^ (W's right operand) and e^G (scale q^) (O's left operand), in place
 #pragma unroll
@@ -577,10 +614,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
     __syncthreads();
 
     // ---------------- state-dependent part, per 16-column strip ----------------
+    // (straight-line MFMA work; the next chunk's elementwise pass follows in the
+    // same block so its VALU work can issue under these MFMAs)
+    bf16x4 ob[SPW][4];
 #pragma unroll
     for (int st = 0; st < SPW; ++st) {
       const int s = wave + 4 * st;
-      if (s >= NS) break;
+      if constexpr (NS < 4) {
+        if (s >= NS) break;
+      }
       const int jl = 16 * s;
       bf16x8 Sb[4];
 #pragma unroll
@@ -592,25 +634,32 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
       for (int rt = 0; rt < 4; ++rt) {
         const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[16 * rt + 4 * g4]);
         N[rt] = bt * to_f32x4(rows4(sm.v, 16 * rt + 4 * g4, jl, l16));
+      }
 #pragma unroll
-        for (int ks = 0; ks < (rt >= 2 ? 2 : 1); ++ks) {
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 Bop = cat(rows4(sm.v, 32 * ks + 8 * g4, jl, l16),
+                               rows4(sm.v, 32 * ks + 8 * g4 + 4, jl, l16));
+#pragma unroll
+        for (int rt = 2 * ks; rt < 4; ++rt) {
           const bf16x8 Aop = *reinterpret_cast<const bf16x8*>(&sm.lb[16 * rt + l16][32 * ks + 8 * g4]);
-          const bf16x8 Bop = cat(rows4(sm.v, 32 * ks + 8 * g4, jl, l16),
-                                 rows4(sm.v, 32 * ks + 8 * g4 + 4, jl, l16));
           N[rt] = mfma32(Aop, Bop, N[rt]);
         }
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) N[rt] = mfma32(perm_row(sm.r2.wn, 16 * rt + l16, 32 * kb, g4), Sb[kb], N[rt]);
       }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          N[rt] = mfma32(perm_row(sm.r2.wn, 16 * rt + l16, 32 * kb, g4), Sb[kb], N[rt]);
 
       // O = (e^G q) S + Mq N
       f32x4 O[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rt = 0; rt < 4; ++rt) O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) O[rt] = mfma32(perm_row(sm.qe, 16 * rt + l16, 32 * kb, g4), Sb[kb], O[rt]);
-      }
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          O[rt] = mfma32(perm_row(sm.qe, 16 * rt + l16, 32 * kb, g4), Sb[kb], O[rt]);
       bf16x8 Nh[2], Nl[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -619,32 +668,23 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
         Nl[kb] = cat(to_bf16x4(N[2 * kb] - to_f32x4(h0)), to_bf16x4(N[2 * kb + 1] - to_f32x4(h1)));
       }
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < (rt >= 2 ? 2 : 1); ++kb)
+        for (int rt = 2 * kb; rt < 4; ++rt)
           O[rt] = mfma32(perm_row(sm.aoff, 16 * rt + l16, 32 * kb, g4), Nh[kb], O[rt]);
-        const bf16x4 ob = to_bf16x4(O[rt]);
-        bf16* orow = reinterpret_cast<bf16*>(outb) + jl + l16;
-        if (L == kC) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            orow[(unsigned)(t0 + 16 * rt + 4 * g4 + j) * (unsigned)rowstride] = ob[j];
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int t = 16 * rt + 4 * g4 + j;
-            if (t < L) orow[(unsigned)(t0 + t) * (unsigned)rowstride] = ob[j];
-          }
-        }
-      }
+      for (int rt = 0; rt < 4; ++rt) ob[st][rt] = to_bf16x4(O[rt]);
 
       // S <- Diag(e^{G_last}) S + (e^{G_last - G} k)^T N, two-term split on both sides
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt) {
         const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.gam[16 * rt + 4 * g4]);
         S[st][rt] *= gm;
+      }
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
           const bf16x8 Ah = cat(rows4(sm.kph, 32 * kb + 4 * g4, 16 * rt, l16),
                                 rows4(sm.kph, 32 * kb + 16 + 4 * g4, 16 * rt, l16));
           const bf16x8 Al = cat(rows4(sm.kpl, 32 * kb + 4 * g4, 16 * rt, l16),
@@ -652,6 +692,35 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
           S[st][rt] = mfma32(Ah, Nh[kb], S[st][rt]);
           S[st][rt] = mfma32(Ah, Nl[kb], S[st][rt]);
           S[st][rt] = mfma32(Al, Nh[kb], S[st][rt]);
+        }
+    }
+
+    // elementwise pass of the next chunk (harmless recomputation after the last
+    // one: nothing reads its results); it writes only rloc/wtot, which this
+    // chunk no longer reads
+    elementwise<VS>(el, pf, Ln, tq, g4, c2, c1, lb2, p.scale, &sm.rloc[wave][ch0],
+                    &sm.wtot[wave][ch0]);
+
+    // outputs (rows of tokens inside the sequence)
+#pragma unroll
+    for (int st = 0; st < SPW; ++st) {
+      const int s = wave + 4 * st;
+      if constexpr (NS < 4) {
+        if (s >= NS) break;
+      }
+      bf16* ocol = reinterpret_cast<bf16*>(outb) + 16 * s + l16;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        if (L == kC) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            ocol[(unsigned)(t0 + 16 * rt + 4 * g4 + j) * (unsigned)rowstride] = ob[st][rt][j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int t = 16 * rt + 4 * g4 + j;
+            if (t < L) ocol[(unsigned)(t0 + t) * (unsigned)rowstride] = ob[st][rt][j];
+          }
         }
       }
     }
