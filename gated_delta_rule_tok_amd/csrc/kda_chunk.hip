@@ -171,7 +171,7 @@ struct Smem {
   float beta[kC];
   float rloc[4][128];   // G at token 7 of each sub-chunk, relative to the sub-chunk start
   float wtot[4][128];   // log-decay total of each sub-chunk
-  float dab[6][128];    // e^{R_a - R_b}, a > b
+  float dab[7][128];    // e^{R_a - R_b}, a > b; row 6 holds ones (diagonal blocks)
   float gam[128];       // e^{G_last}
 };
 
@@ -447,51 +447,63 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
       for (int w = bb; w < a; ++w) d += sm.wtot[w][c];
       sm.dab[pr][c] = ex2(d);
     }
+    if (tid < 128) sm.dab[6][tid] = 1.f;
     if (tid < 128) sm.gam[tid] = ex2(sm.wtot[0][tid] + sm.wtot[1][tid] + sm.wtot[2][tid] + sm.wtot[3][tid]);
     __syncthreads();
 
     // ---------------- A and Mq blocks (bf16 MFMA over the 128 channels) ----------------
-    f32x4 Mreg[3];
+    // wave w takes pairs w, w+4, w+8 of the 10 lower blocks; waves 2 and 3 repeat
+    // pair 9 as a third, discarded pair so the compute stays branch-free
+    f32x4 accA[3], accM[3];
 #pragma unroll
     for (int k3 = 0; k3 < 3; ++k3) {
-      const int pi = wave + 4 * k3;
-      Mreg[k3] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (pi >= 10) continue;
+      const int pi = min(wave + 4 * k3, 9);
       int a, bb;
       pair_ab(pi, a, bb);
-      f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
+      const float* drow = &sm.dab[bb < a ? (a * (a - 1)) / 2 + bb : 6][0];  // row 6: ones
+      accA[k3] = accM[k3] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int c0 = 32 * ks + 8 * g4;
         const bf16x8 aK = *reinterpret_cast<const bf16x8*>(&sm.ke[16 * a + l16][c0]);
         const bf16x8 aQ = *reinterpret_cast<const bf16x8*>(&sm.qe[16 * a + l16][c0]);
-        bf16x8 bK = *reinterpret_cast<const bf16x8*>(&sm.r2.kf[16 * bb + l16][c0]);
-        if (bb < a) {
-          const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.dab[(a * (a - 1)) / 2 + bb][c0]);
-          const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.dab[(a * (a - 1)) / 2 + bb][c0 + 4]);
-          float f[8];
+        const bf16x8 bK = *reinterpret_cast<const bf16x8*>(&sm.r2.kf[16 * bb + l16][c0]);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(drow + c0);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(drow + c0 + 4);
+        float f[8];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            f[i] = (float)bK[i] * d0[i];
-            f[4 + i] = (float)bK[4 + i] * d1[i];
-          }
-          bK = pack8(f);
+        for (int i = 0; i < 4; ++i) {
+          f[i] = (float)bK[i] * d0[i];
+          f[4 + i] = (float)bK[4 + i] * d1[i];
         }
-        accA = mfma32(aK, bK, accA);
-        accM = mfma32(aQ, bK, accM);
+        const bf16x8 bKd = pack8(f);
+        accA[k3] = mfma32(aK, bKd, accA[k3]);
+        accM[k3] = mfma32(aQ, bKd, accM[k3]);
       }
+    }
+    f32x4 Mreg[3];
+#pragma unroll
+    for (int k3 = 0; k3 < 3; ++k3) {
+      const int pi = wave + 4 * k3;
+      int a, bb;
+      pair_ab(min(pi, 9), a, bb);
       f32x4 at;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * g4 + j;  // row inside the block
         const bool keepA = bb < a || l16 < r;
         const bool keepM = bb < a || l16 <= r;
-        const float av = keepA ? accA[j] * sm.beta[16 * a + r] : 0.f;
-        at[j] = av;
-        if (bb < a) sm.aoff[16 * a + r][16 * bb + l16] = (bf16)av;
-        Mreg[k3][j] = keepM ? accM[j] : 0.f;
+        at[j] = keepA ? accA[k3][j] * sm.beta[16 * a + r] : 0.f;
+        Mreg[k3][j] = keepM ? accM[k3][j] : 0.f;
       }
-      if (bb == a) *reinterpret_cast<f32x4*>(&sm.adt[a][l16][4 * g4]) = at;
+      if (pi < 10) {
+        if (bb == a) {
+          *reinterpret_cast<f32x4*>(&sm.adt[a][l16][4 * g4]) = at;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sm.aoff[16 * a + 4 * g4 + j][16 * bb + l16] = (bf16)at[j];
+        }
+      }
     }
     __syncthreads();
 
