@@ -92,7 +92,7 @@ const char* kda_status_string(kda_status_t status) {
 const char* kda_last_hip_error(void) { return t_last_hip_error; }
 
 int kda_debug_set_kernel(int k) {
-  if (k < 0 || k > 2) return -1;
+  if (k < 0 || k > 2) return -1;  // 0 pipelined 16-token, 1 64-token chunk, 2 token-serial
   return g_kernel_override.exchange(k);
 }
 
@@ -154,12 +154,16 @@ kda_status_t kda_chunk_prefill_fwd(const void* q, const void* k, const void* v, 
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (hipError_t e = kda::launch_plan(p, st); e != hipSuccess) return hip_failure(e, "plan launch");
-  if (g_kernel_override.load(std::memory_order_relaxed) == 2) {
+  const int kernel = g_kernel_override.load(std::memory_order_relaxed);
+  if (kernel == 2) {
     if (hipError_t e = kda::launch_recurrent(p, st); e != hipSuccess)
       return hip_failure(e, "token-serial kernel launch");
-  } else {
+  } else if (kernel == 1) {
     if (hipError_t e = kda::launch_chunk(p, st); e != hipSuccess)
-      return hip_failure(e, "chunk kernel launch");
+      return hip_failure(e, "64-token chunk kernel launch");
+  } else {
+    if (hipError_t e = kda::launch_pipe(p, st); e != hipSuccess)
+      return hip_failure(e, "pipelined chunk kernel launch");
   }
   return KDA_OK;
 }

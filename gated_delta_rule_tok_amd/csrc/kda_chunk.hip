@@ -46,21 +46,13 @@
 //    row-major [token][channel] array.  So every operand stays row-major.
 //  * v_permlane16_swap / v_permlane32_swap exchange 16-lane rows and 32-lane
 //    halves; they carry the cumulative-sum scan across the rows of a wave.
-#include "kda_internal.h"
+#include "kda_mfma.h"
 
 namespace kda {
 namespace {
 
-typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kThreads = 256;
 constexpr int kC = 64;  // tokens per chunk
-constexpr float kLog2e = 1.4426950408889634f;
 
 // LDS row strides in bf16 elements, chosen for the access each array sees:
 constexpr int kRowA = 136;  // 68 dwords = 4 mod 32: 16-row 16-byte operand reads
@@ -68,34 +60,6 @@ constexpr int kRowT = 144;  // 72 dwords = 8 mod 32: transpose reads (4 rows x 3
 constexpr int kRowW = 132;  // 66 dwords = 2 mod 32: 16-row 8-byte operand reads
 constexpr int kRowM = 68;   // 64 x 64 token-token matrices read 8 bytes per row
 constexpr int kRowL = 72;   // 64 x 64 read 16 bytes per row
-
-__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-
-__device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
-  return bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-}
-__device__ __forceinline__ f32x4 to_f32x4(bf16x4 v) {
-  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-}
-__device__ __forceinline__ bf16x8 pack8(const float* f) {
-  return bf16x8{(bf16)f[0], (bf16)f[1], (bf16)f[2], (bf16)f[3],
-                (bf16)f[4], (bf16)f[5], (bf16)f[6], (bf16)f[7]};
-}
-__device__ __forceinline__ void unpack8(uint4 u, float* f) {
-  f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
-  f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
-}
 
 // Sum over the 16 lanes of a DPP row (all 16 lanes get the same bits).
 __device__ __forceinline__ float row_sum16(float x) {
@@ -118,13 +82,6 @@ __device__ __forceinline__ float rows_exclusive_sum(float x, int row) {
   const auto s32 = __builtin_amdgcn_permlane32_swap(up, up, false, false);
   const float low_pair = __uint_as_float(s32[0]);  // rows 2, 3: t0 + t1
   return (odd ? from_prev_row : 0.f) + (row >= 2 ? low_pair : 0.f);
-}
-
-// Transposed 8-byte LDS read (see the header comment): pointer of this lane.
-__device__ __forceinline__ bf16x4 tr4(const bf16* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p));
-  return __builtin_bit_cast(bf16x4, v);
 }
 
 // Operand with k over 4 consecutive rows base.. and lane column c0 + l16 of a

@@ -65,4 +65,9 @@ hipError_t launch_recurrent(const Params& p, hipStream_t stream);
 // (sequence, head, V-slice).
 hipError_t launch_chunk(const Params& p, hipStream_t stream);
 
+// Pipelined 16-token chunk forward: producer waves build each chunk's
+// state-independent operands ahead of the state waves, one workgroup per
+// (sequence, head, V-slice).
+hipError_t launch_pipe(const Params& p, hipStream_t stream);
+
 }  // namespace kda

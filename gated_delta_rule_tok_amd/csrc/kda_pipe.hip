@@ -1,0 +1,559 @@
+// kda_pipe.hip -- KDA chunked-prefill forward for gfx950 on 16-token chunks,
+// with the state-independent work of each chunk produced ahead of the serial
+// state pass by other waves of the same workgroup.
+//
+// The method is the bounded-gate, normalised-q/k delta rule of vLLM PR
+// #55737's report ("Features and motivation"):
+//   S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,  o_t = scale S_t^T q_t,
+// with log a_t = lower_bound * sigmoid(exp(A_log) (g_t + dt_bias)), b_t =
+// sigmoid(beta logit) and q, k L2-normalised.  Unrolled over a chunk with G the
+// inclusive cumulative log-decay (per key channel) and S the state entering it:
+//   A[t,i] = b_t sum_c k_t[c] k_i[c] e^{G_t[c]-G_i[c]}        (i < t)
+//   M[t,i] = scale sum_c q_t[c] k_i[c] e^{G_t[c]-G_i[c]}       (i <= t)
+//   N = (I + A)^-1 diag(b) (V - (e^G k) S)
+//   O = scale (e^G q) S + M N
+//   S <- Diag(e^{G_last}) S + (e^{G_last - G} k)^T N
+//
+// Work split.  One workgroup per (sequence, head, value slice).  Waves 0-3
+// ("producers") each take every fourth 16-token chunk and build the chunk's
+// package in LDS: the gate, the cumulative decay, the decayed operands, the
+// 16x16 products A and M, the inverse (I + A)^-1, and the norms.  None of it
+// depends on the state.  The remaining waves ("state waves", one or two
+// 16-column strips of the value slice each) walk the chunks in order, keeping
+// their strip of S (128 x 16 fp32) in registers, and apply the three state
+// contractions and the output.  Packages are double-buffered per round of
+// four chunks: in round r the producers write round r while the state waves
+// read round r-1; one workgroup barrier ends each round.  On gfx950 this puts
+// a VALU-heavy producer wave and an MFMA-heavy state wave on every SIMD.
+//
+// Norms are applied after the products, as row/column scalings: k and q enter
+// the MFMAs raw; 1/||k_t|| is read off the diagonal of the A product
+// (sum_c k_t[c] e^{x} k_t[c] e^{-x}), scale/||q_t|| comes from a separate
+// pass over q.  With rk = 1/||k|| and rqs = scale/||q||:
+//   A[t,i] = b_t rk_t rk_i (K_E K_F^T)[t,i],  M'[t,i] = rqs_t (Q_E K_F^T)[t,i]
+//   D = V - rk (X S),  N = diag(b) D + L D,  N' = rk N
+//   O = rqs (Q_T S) + M' N',  S <- Diag(e^{G_last}) S + K'^T N'
+// with X = e^G k, Q_T = e^G q, K' = e^{G_last - G} k (raw k, q) and
+// L = ((I + A)^-1 - I) diag(b).
+//
+// Exponent ranges.  The products A and M use a reference R = G at token 7
+// (K_E = k e^{G-R}, Q_E = q e^{G-R}, K_F = k e^{R-G}): every factor stays within
+// 2^{+-8 |lower_bound| log2 e}, far from fp32/bf16 under- and overflow, so
+// small k entries keep their relative precision.  The state-side operands use
+// the chunk start (X, Q_T <= |k|, |q|) and the chunk end (K' <= |k|); where
+// those underflow the true contribution is below 2^-126 of the state.
+//
+// Precision (checked against the fp64 recurrence on the workloads'
+// distributions): bf16 MFMA operands with fp32 accumulation; the inverse by
+// MFMA doubling on the 16x16 block; the unit diagonal of (I + A)^-1 diag(b)
+// applied in fp32; the state update with a two-term (hi + lo) bf16 split of
+// both operands (three products), so the fp32 state does not pick up bf16
+// rounding each chunk.
+#include "kda_mfma.h"
+
+namespace kda {
+namespace {
+
+constexpr int kTok = 16;  // tokens per chunk
+constexpr int kPW = 4;    // producer waves = chunks per round
+
+template <int VS>
+struct Cfg {
+  static constexpr int NS = VS / 16;             // 16-column strips in the slice
+  static constexpr int NSW = NS < 4 ? NS : 4;    // state waves
+  static constexpr int SPW = NS / NSW;           // strips per state wave
+  static constexpr int kThreads = 64 * (kPW + NSW);
+};
+
+// [128][16] tiles (row = key channel, column = token): rows are stored in the
+// order swz(r), which keeps both the producers' 16-byte row writes (8 lanes
+// write rows 4c + i, c = 0..3, two halves each) and the transposed operand
+// reads (4 consecutive rows x 32 bytes) on distinct banks.
+__device__ __forceinline__ int swz(int r) { return r ^ ((r >> 2) & 3); }
+
+// Fragment tiles: the A-operand order of a 16x16x16 MFMA.  Element (row m,
+// column k) of 16x16 block b sits at (b * 64) + ((k / 4) * 16 + m) * 4 + k % 4,
+// so lane (l16, g4) reads its four k-values as 8 contiguous bytes and a wave
+// reads one block as 512 contiguous bytes.
+__device__ __forceinline__ int frag(int blk, int m, int k) {
+  return blk * 256 + ((k >> 2) * 16 + m) * 4 + (k & 3);
+}
+
+// One chunk's package: written by one producer wave, read by the state waves.
+struct Pack {
+  bf16 x[128 * kTok];    // e^{G} k, swizzled rows; scratch before that: Q_E
+  bf16 qt[128 * kTok];   // e^{G} q, swizzled rows
+  bf16 kph[128 * kTok];  // K' high part, fragment order (block = 16 keys); scratch: K_E
+  bf16 kpl[128 * kTok];  // K' low part; scratch: K_F
+  bf16 l[256];           // L, fragment order
+  bf16 m[256];           // M', fragment order
+  float beta[kTok];
+  float rk[kTok];        // 1 / ||k_t||
+  float rqs[kTok];       // scale / ||q_t||
+  float gam[128];        // e^{G_last}
+};
+
+// Raw inputs of one chunk for one producer lane: tokens 8 th + rr of channels
+// 4 cg .. 4 cg + 3 (cg = lane / 2, th = lane % 2); q again as rows for the
+// norm (token lane / 4, channels 32 (lane % 4) ..); the beta logit of token
+// `lane` (lanes < 16).
+struct Raw {
+  uint2 q[8], k[8], g[8];
+  uint4 qn[4];
+  uint32_t beta;
+};
+
+__device__ __forceinline__ void load_raw(Raw& r, const uint16_t* qb, const uint16_t* kb,
+                                         const uint16_t* gb, const uint16_t* bb, int rowstride,
+                                         int H, int t0, int Lc, int lane) {
+  const unsigned ch = 4u * unsigned(lane >> 1);
+  const int th = lane & 1;
+  if (Lc == kTok) {
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const unsigned off = unsigned(t0 + 8 * th + rr) * unsigned(rowstride) + ch;
+      r.q[rr] = *reinterpret_cast<const uint2*>(qb + off);
+      r.k[rr] = *reinterpret_cast<const uint2*>(kb + off);
+      r.g[rr] = *reinterpret_cast<const uint2*>(gb + off);
+    }
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      if (8 * th + rr < Lc) {
+        const unsigned off = unsigned(t0 + 8 * th + rr) * unsigned(rowstride) + ch;
+        r.q[rr] = *reinterpret_cast<const uint2*>(qb + off);
+        r.k[rr] = *reinterpret_cast<const uint2*>(kb + off);
+        r.g[rr] = *reinterpret_cast<const uint2*>(gb + off);
+      } else {
+        r.q[rr] = r.k[rr] = r.g[rr] = uint2{0u, 0u};
+      }
+    }
+  }
+  const int tn = lane >> 2;
+  if (tn < Lc) {
+    const unsigned off = unsigned(t0 + tn) * unsigned(rowstride) + 32u * unsigned(lane & 3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.qn[i] = *reinterpret_cast<const uint4*>(qb + off + 8 * i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.qn[i] = uint4{0u, 0u, 0u, 0u};
+  }
+  r.beta = lane < Lc ? uint32_t(bb[unsigned(t0 + lane) * unsigned(H)]) : 0u;
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, a), c, false);
+}
+
+__device__ __forceinline__ uint32_t pk2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, bf16x2{(bf16)lo, (bf16)hi});
+}
+
+// Channel i (0..3) of a 4-channel bf16 group.
+__device__ __forceinline__ float chan(uint2 w, int i) {
+  const uint32_t d = i < 2 ? w.x : w.y;
+  return (i & 1) ? bf16_hi(d) : bf16_lo(d);
+}
+
+// Values a producer keeps in registers across its MFMA step: X and the two
+// parts of K', packed bf16 pairs of consecutive tokens, per channel.
+struct Held {
+  uint32_t x[4][4], kh[4][4], kl[4][4];
+};
+
+// Producer, first half: norms of q, beta, the gate and its cumulative sum,
+// and every decayed operand.  Writes Q_T, the scratch operands of the A / M
+// products, gam, beta and rqs; returns X and K' in `held`.  FULL: all 16
+// tokens are inside the sequence (no masking).
+template <bool FULL>
+__device__ __forceinline__ void produce_operands(Pack& pk, const Raw& raw, Held& held, int Lc,
+                                                 int lane, const float* c2, float c1, float lb2,
+                                                 float scale) {
+  const int cg = lane >> 1, th = lane & 1;
+
+  // scale / ||q_t|| for token lane/4: four lanes hold 32 channels each
+  {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s = dot2(raw.qn[i].x, s);
+      s = dot2(raw.qn[i].y, s);
+      s = dot2(raw.qn[i].z, s);
+      s = dot2(raw.qn[i].w, s);
+    }
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0xB1, 0xF, 0xF, false));
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x4E, 0xF, 0xF, false));
+    if ((lane & 3) == 0) pk.rqs[lane >> 2] = rsqrtf(s + kNormEps) * scale;
+    if (lane < kTok)
+      pk.beta[lane] = lane < Lc ? rcp(1.f + ex2(-kLog2e * bf16_to_f32(uint16_t(raw.beta)))) : 0.f;
+  }
+
+  // gate sigma per (token, channel) and its running sum over this lane's 8
+  // tokens; the log2 decay of a token is lb2 * sigma (lb2 = lower_bound log2 e)
+  float cs[4][8];
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) {
+    const bool valid = FULL || 8 * th + rr < Lc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float sg = rcp(1.f + ex2(fmaf(chan(raw.g[rr], i), c1, c2[i])));
+      const float inc = valid ? sg : 0.f;
+      cs[i][rr] = rr == 0 ? inc : cs[i][rr - 1] + inc;
+    }
+  }
+
+  // R = G at token 7.  Lane th = 0 holds tokens 0..7 (G_t - R = lb2 (cs_t - cs_7)),
+  // lane th = 1 tokens 8..15 (G_t - R = lb2 cs_t); the partner lane supplies
+  // the other half's total.
+  float off[4], eR[4], eLR[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float own = cs[i][7], other = pair_swap(own);
+    const float s7 = th ? other : own;    // sigma sum of tokens 0..7
+    const float s15 = th ? own : other;   // sigma sum of tokens 8..15
+    off[i] = th ? 0.f : -lb2 * own;
+    eR[i] = ex2(lb2 * s7);                // e^{R} (chunk start to token 7)
+    eLR[i] = ex2(lb2 * s15);              // e^{G_last - R}
+  }
+  if (th == 0)
+    *reinterpret_cast<f32x4*>(&pk.gam[4 * cg]) =
+        f32x4{eR[0] * eLR[0], eR[1] * eLR[1], eR[2] * eLR[2], eR[3] * eLR[3]};
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = swz(4 * cg + i) * kTok + 8 * th;  // this lane's 8 tokens of channel 4cg+i
+    uint32_t ke[4], kf[4], qe[4], qt[4];
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+      float vke[2], vkf[2], vqe[2], vqt[2], vx[2], vkp[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int rr = 2 * pr + h;
+        const float x = fmaf(cs[i][rr], lb2, off[i]);  // G - R
+        const float E = ex2(x), F = ex2(-x);
+        const float kv = chan(raw.k[rr], i), qv = chan(raw.q[rr], i);
+        vke[h] = kv * E;
+        vkf[h] = kv * F;
+        vqe[h] = qv * E;
+        vqt[h] = vqe[h] * eR[i];
+        vx[h] = vke[h] * eR[i];
+        vkp[h] = vkf[h] * eLR[i];
+      }
+      ke[pr] = pk2(vke[0], vke[1]);
+      kf[pr] = pk2(vkf[0], vkf[1]);
+      qe[pr] = pk2(vqe[0], vqe[1]);
+      qt[pr] = pk2(vqt[0], vqt[1]);
+      held.x[i][pr] = pk2(vx[0], vx[1]);
+      const uint32_t hi = pk2(vkp[0], vkp[1]);
+      held.kh[i][pr] = hi;
+      held.kl[i][pr] = pk2(vkp[0] - bf16_lo(hi), vkp[1] - bf16_hi(hi));
+    }
+    *reinterpret_cast<uint4*>(&pk.kph[row]) = uint4{ke[0], ke[1], ke[2], ke[3]};
+    *reinterpret_cast<uint4*>(&pk.kpl[row]) = uint4{kf[0], kf[1], kf[2], kf[3]};
+    *reinterpret_cast<uint4*>(&pk.x[row]) = uint4{qe[0], qe[1], qe[2], qe[3]};
+    *reinterpret_cast<uint4*>(&pk.qt[row]) = uint4{qt[0], qt[1], qt[2], qt[3]};
+  }
+}
+
+// Producer, second half: the A and M products, 1/||k||, the inverse and L,
+// then X and K' over the scratch operands (this wave's own LDS accesses are
+// processed in order, so the scratch reads are done before they are
+// overwritten).
+__device__ __forceinline__ void produce_products(Pack& pk, const Held& held, int lane) {
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int cg = lane >> 1, th = lane & 1;
+
+  // A = K_E K_F^T, A^T = K_F K_E^T and M'^T = K_F Q_E^T over the 128 channels;
+  // k-slots 8 g4 .. 8 g4 + 7 of each 32-channel block, on both sides
+  __builtin_amdgcn_wave_barrier();  // the operands were written by other lanes of this wave
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 accA = zero, accAt = zero, accMt = zero;
+  const int col = 4 * (l16 & 3);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int r1 = 32 * kb + 8 * g4 + (l16 >> 2), r2 = r1 + 4;
+    const int o1 = swz(r1) * kTok + col, o2 = swz(r2) * kTok + col;
+    const bf16x8 KE = cat(tr4(&pk.kph[o1]), tr4(&pk.kph[o2]));
+    const bf16x8 KF = cat(tr4(&pk.kpl[o1]), tr4(&pk.kpl[o2]));
+    const bf16x8 QE = cat(tr4(&pk.x[o1]), tr4(&pk.x[o2]));
+    accA = mfma32(KE, KF, accA);     // [t = 4g4+j][i = l16]
+    accAt = mfma32(KF, KE, accAt);   // [i = 4g4+j][t = l16]
+    accMt = mfma32(KF, QE, accMt);   // [i = 4g4+j][t = l16]
+  }
+
+  // 1/||k_t|| from the diagonal (lane l16 of group l16/4 holds element (l16, l16))
+  {
+    const int jd = l16 & 3;
+    const float dg = jd == 0 ? accA[0] : jd == 1 ? accA[1] : jd == 2 ? accA[2] : accA[3];
+    if (g4 == (l16 >> 2)) pk.rk[l16] = rsqrtf(dg + kNormEps);
+  }
+  __builtin_amdgcn_wave_barrier();  // rk, beta, rqs were written by other lanes of this wave
+  const f32x4 bR = *reinterpret_cast<const f32x4*>(&pk.beta[4 * g4]);
+  const f32x4 rkR = *reinterpret_cast<const f32x4*>(&pk.rk[4 * g4]);
+  const float bC = pk.beta[l16], rkC = pk.rk[l16], rqC = pk.rqs[l16];
+
+  f32x4 Nn, Nt, Mv, I4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 4 * g4 + j;
+    Nn[j] = l16 < r ? bR[j] * rkR[j] * rkC * accA[j] : 0.f;    // A[r][l16]
+    Nt[j] = r < l16 ? bC * rkC * rkR[j] * accAt[j] : 0.f;      // A[l16][r]
+    Mv[j] = r <= l16 ? rqC * accMt[j] : 0.f;                   // M'[l16][r]
+    I4[j] = r == l16 ? 1.f : 0.f;
+  }
+  *reinterpret_cast<bf16x4*>(&pk.m[frag(0, l16, 4 * g4)]) = to_bf16x4(Mv);
+
+  // (I + A)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8) (A^16 = 0).  Each product is
+  // formed together with its transpose: an accumulator holds Z[4g+j][l16],
+  // which is Z's B-operand layout and Z^T's A-operand layout, so Z = X Y is
+  // mfma(X^T, Y) and Z^T = Y^T X^T is mfma(Y, X^T).
+  {
+    const bf16x4 nb = to_bf16x4(Nn), ntb = to_bf16x4(Nt);
+    const f32x4 N2 = mfma16(ntb, nb, zero), N2t = mfma16(nb, ntb, zero);
+    const bf16x4 n2b = to_bf16x4(N2), n2tb = to_bf16x4(N2t);
+    const f32x4 N4 = mfma16(n2tb, n2b, zero), N4t = mfma16(n2b, n2tb, zero);
+    const bf16x4 n4b = to_bf16x4(N4), n4tb = to_bf16x4(N4t);
+    const f32x4 N8 = mfma16(n4tb, n4b, zero);
+    const f32x4 P1t = mfma16(n2b, to_bf16x4(-Nt), I4 - Nt + N2t);   // (I - A)(I + A^2)
+    const bf16x4 p1tb = to_bf16x4(P1t);
+    const f32x4 P2t = mfma16(n4b, p1tb, P1t);                        // ... (I + A^4)
+    const bf16x4 p2tb = to_bf16x4(P2t), n8b = to_bf16x4(N8);
+    const f32x4 Dt = mfma16(n8b, p2tb, P2t);                         // D^T: D[l16][4g4+j]
+    // L[t][i] = (D - I)[t][i] b_i at fragment (m = t = l16, k = i = 4g4 + j)
+    *reinterpret_cast<bf16x4*>(&pk.l[frag(0, l16, 4 * g4)]) = to_bf16x4((Dt - I4) * bR);
+  }
+
+  // X over Q_E, K' over K_E / K_F (after every lane's operand reads above)
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = 4 * cg + i;
+    *reinterpret_cast<uint4*>(&pk.x[swz(c) * kTok + 8 * th]) =
+        uint4{held.x[i][0], held.x[i][1], held.x[i][2], held.x[i][3]};
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int o = frag(c >> 4, c & 15, 8 * th + 4 * hh);
+      *reinterpret_cast<uint2*>(&pk.kph[o]) = uint2{held.kh[i][2 * hh], held.kh[i][2 * hh + 1]};
+      *reinterpret_cast<uint2*>(&pk.kpl[o]) = uint2{held.kl[i][2 * hh], held.kl[i][2 * hh + 1]};
+    }
+  }
+}
+
+// Value strip of one chunk for a state lane: tokens 4 g4 + j, one column.
+__device__ __forceinline__ uint2 load_v4(const uint16_t* vcol, int rowstride, int t0, int Lc,
+                                         int g4) {
+  uint16_t e[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = 4 * g4 + j;
+    e[j] = t < Lc ? vcol[unsigned(t0 + t) * unsigned(rowstride)] : uint16_t(0);
+  }
+  return uint2{uint32_t(e[0]) | (uint32_t(e[1]) << 16), uint32_t(e[2]) | (uint32_t(e[3]) << 16)};
+}
+
+template <int VS>
+__global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
+  using C = Cfg<VS>;
+  constexpr int SPW = C::SPW, NSW = C::NSW;
+  __shared__ __attribute__((aligned(16))) Pack pk[2][kPW];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a uniform (scalar) value: the two roles below run separate
+  // loops, each with one barrier per round
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+
+  // workgroup -> (sequence rank, head, slice); the slices of one head stay on
+  // one XCD so they share q/k/g in its L2
+  int b = blockIdx.x;
+  const int G = gridDim.x;
+  if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
+  const int slice = b % p.vsplit;
+  const int rest = b / p.vsplit;
+  const int h = rest % p.H;
+  const int n = p.order[rest / p.H];
+  const int H = p.H;
+
+  const int bos = min(max(p.cu[n], 0), p.T);
+  const int eos = min(max(p.cu[n + 1], bos), p.T);
+  const int nc = (eos - bos + kTok - 1) / kTok;  // chunks
+  const int nr = (nc + kPW - 1) / kPW;            // rounds
+  const int rowstride = H * kD;
+
+  if (wave < kPW) {
+    // ---------------- producer waves ----------------
+    const uint16_t* qb = p.q + size_t(h) * kD;
+    const uint16_t* kb = p.k + size_t(h) * kD;
+    const uint16_t* gb = p.g + size_t(h) * kD;
+    const uint16_t* betab = p.beta + h;
+    const float eA = expf(p.A_log[h]);
+    const float c1 = -kLog2e * eA;
+    const float lb2 = p.lower_bound * kLog2e;
+    float c2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c2[i] = c1 * p.dt_bias[h * kD + 4 * (lane >> 1) + i];
+    Raw raw;
+    if (wave < nc) {
+      const int t0 = bos + kTok * wave;
+      load_raw(raw, qb, kb, gb, betab, rowstride, H, t0, min(kTok, eos - t0), lane);
+    }
+    for (int r = 0; r <= nr; ++r) {
+      const int j = kPW * r + wave;
+      if (r < nr && j < nc) {
+        const int t0 = bos + kTok * j, Lc = min(kTok, eos - t0);
+        Pack& P = pk[r & 1][wave];
+        Held held;
+        if (Lc == kTok) produce_operands<true>(P, raw, held, Lc, lane, c2, c1, lb2, p.scale);
+        else produce_operands<false>(P, raw, held, Lc, lane, c2, c1, lb2, p.scale);
+        // this wave's next chunk, one round ahead
+        const int tn = t0 + kTok * kPW;
+        if (tn < eos) load_raw(raw, qb, kb, gb, betab, rowstride, H, tn, min(kTok, eos - tn), lane);
+        produce_products(P, held, lane);
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ---------------- state waves ----------------
+  // S[u][rt][j] = S[16 rt + 4 g4 + j][column of strip u]
+  const int sw = wave - kPW;
+  const int colb = slice * VS + 16 * sw + l16;  // column of strip 0; strip u adds 16 NSW u
+  const uint16_t* vb = p.v + size_t(h) * kD + colb;
+  uint16_t* ob = p.out + size_t(h) * kD + colb;
+  const size_t sbase = (size_t(n) * H + h) * kD * kD;
+  f32x4 S[SPW][8];
+#pragma unroll
+  for (int u = 0; u < SPW; ++u)
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if (p.s0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const size_t idx = sbase + size_t(16 * rt + 4 * g4 + j) * kD + colb + 16 * NSW * u;
+          x[j] = p.state_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p.s0)[idx])
+                              : static_cast<const float*>(p.s0)[idx];
+        }
+      }
+      S[u][rt] = x;
+    }
+  uint2 vnext[kPW][SPW], vcur[kPW][SPW];
+#pragma unroll
+  for (int c = 0; c < kPW; ++c)
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) vnext[c][u] = uint2{0u, 0u};
+
+  for (int r = 0; r <= nr; ++r) {
+    // values of this round's chunks (consumed next round)
+#pragma unroll
+    for (int c = 0; c < kPW; ++c)
+#pragma unroll
+      for (int u = 0; u < SPW; ++u) {
+        vcur[c][u] = vnext[c][u];
+        const int t0 = bos + kTok * (kPW * r + c);
+        vnext[c][u] = r < nr && t0 < eos
+                          ? load_v4(vb + 16 * NSW * u, rowstride, t0, min(kTok, eos - t0), g4)
+                          : uint2{0u, 0u};
+      }
+    if (r >= 1) {
+#pragma unroll
+      for (int c = 0; c < kPW; ++c) {
+        const int j = kPW * (r - 1) + c;
+        if (j >= nc) break;
+        const Pack& P = pk[(r - 1) & 1][c];
+        const int t0 = bos + kTok * j, Lc = min(kTok, eos - t0);
+
+        // X and Q_T as A operands; k-slots {32kb + 4g4 + j, 32kb + 16 + 4g4 + j}
+        // match the B operand built from two accumulator tiles of S
+        bf16x8 ax[4], aq[4];
+        const int col = 4 * (l16 & 3);
+#pragma unroll
+        for (int kb2 = 0; kb2 < 4; ++kb2) {
+          const int r1 = 32 * kb2 + 4 * g4 + (l16 >> 2), r2 = r1 + 16;
+          const int o1 = swz(r1) * kTok + col, o2 = swz(r2) * kTok + col;
+          ax[kb2] = cat(tr4(&P.x[o1]), tr4(&P.x[o2]));
+          aq[kb2] = cat(tr4(&P.qt[o1]), tr4(&P.qt[o2]));
+        }
+        const f32x4 bR = *reinterpret_cast<const f32x4*>(&P.beta[4 * g4]);
+        const f32x4 rkR = *reinterpret_cast<const f32x4*>(&P.rk[4 * g4]);
+        const f32x4 rqR = *reinterpret_cast<const f32x4*>(&P.rqs[4 * g4]);
+        const bf16x4 Lf = *reinterpret_cast<const bf16x4*>(&P.l[frag(0, l16, 4 * g4)]);
+        const bf16x4 Mf = *reinterpret_cast<const bf16x4*>(&P.m[frag(0, l16, 4 * g4)]);
+
+#pragma unroll
+        for (int u = 0; u < SPW; ++u) {
+          bf16x8 Sb[4];
+#pragma unroll
+          for (int kb2 = 0; kb2 < 4; ++kb2)
+            Sb[kb2] = cat(to_bf16x4(S[u][2 * kb2]), to_bf16x4(S[u][2 * kb2 + 1]));
+          f32x4 Y = {0.f, 0.f, 0.f, 0.f}, Q = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb2 = 0; kb2 < 4; ++kb2) {
+            Y = mfma32(ax[kb2], Sb[kb2], Y);
+            Q = mfma32(aq[kb2], Sb[kb2], Q);
+          }
+          const uint2 vw = vcur[c][u];
+          const f32x4 V = {bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y)};
+          const f32x4 D = V - rkR * Y;
+          const f32x4 N = mfma16(Lf, to_bf16x4(D), bR * D);
+          const f32x4 Np = rkR * N;
+          const bf16x4 Nh = to_bf16x4(Np);
+          const bf16x4 Nl = to_bf16x4(Np - to_f32x4(Nh));
+          const f32x4 O = mfma16(Mf, Nh, rqR * Q);
+          bf16* orow = reinterpret_cast<bf16*>(ob) + 16 * NSW * u;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int t = 4 * g4 + jj;
+            if (t < Lc) orow[unsigned(t0 + t) * unsigned(rowstride)] = (bf16)O[jj];
+          }
+          // S <- Diag(e^{G_last}) S + K'^T N', two-term split on both sides
+#pragma unroll
+          for (int rt = 0; rt < 8; ++rt) {
+            const f32x4 gm = *reinterpret_cast<const f32x4*>(&P.gam[16 * rt + 4 * g4]);
+            const bf16x4 ah = *reinterpret_cast<const bf16x4*>(&P.kph[frag(rt, l16, 4 * g4)]);
+            const bf16x4 al = *reinterpret_cast<const bf16x4*>(&P.kpl[frag(rt, l16, 4 * g4)]);
+            f32x4 s = S[u][rt] * gm;
+            s = mfma16(ah, Nh, s);
+            s = mfma16(ah, Nl, s);
+            s = mfma16(al, Nh, s);
+            S[u][rt] = s;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // final state
+#pragma unroll
+  for (int u = 0; u < SPW; ++u)
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const size_t idx = sbase + size_t(16 * rt + 4 * g4 + j) * kD + colb + 16 * NSW * u;
+        if (p.state_bf16) static_cast<bf16*>(p.sT)[idx] = (bf16)S[u][rt][j];
+        else static_cast<float*>(p.sT)[idx] = S[u][rt][j];
+      }
+}
+
+}  // namespace
+
+hipError_t launch_pipe(const Params& p, hipStream_t stream) {
+  const void* fn = nullptr;
+  int threads = 0;
+  switch (kD / p.vsplit) {
+    case 128: fn = reinterpret_cast<const void*>(&pipe_kernel<128>); threads = Cfg<128>::kThreads; break;
+    case 64: fn = reinterpret_cast<const void*>(&pipe_kernel<64>); threads = Cfg<64>::kThreads; break;
+    case 32: fn = reinterpret_cast<const void*>(&pipe_kernel<32>); threads = Cfg<32>::kThreads; break;
+    case 16: fn = reinterpret_cast<const void*>(&pipe_kernel<16>); threads = Cfg<16>::kThreads; break;
+    default: return hipErrorInvalidValue;
+  }
+  Params arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel(fn, dim3(p.N * p.H * p.vsplit), dim3(threads), args, 0, stream);
+}
+
+}  // namespace kda
