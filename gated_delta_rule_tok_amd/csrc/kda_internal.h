@@ -67,7 +67,9 @@ hipError_t launch_chunk(const Params& p, hipStream_t stream);
 
 // Pipelined 16-token chunk forward: producer waves build each chunk's
 // state-independent operands ahead of the state waves, one workgroup per
-// (sequence, head, V-slice).
+// (sequence, head, V-slice).  Requires lower_bound >= kPipeLowerBoundMin and a
+// value slice of at most 64 columns (vsplit >= 2).
+constexpr float kPipeLowerBoundMin = -5.0f;
 hipError_t launch_pipe(const Params& p, hipStream_t stream);
 
 }  // namespace kda

@@ -30,18 +30,19 @@
 // the MFMAs raw; 1/||k_t|| is read off the diagonal of the A product
 // (sum_c k_t[c] e^{x} k_t[c] e^{-x}), scale/||q_t|| comes from a separate
 // pass over q.  With rk = 1/||k|| and rqs = scale/||q||:
-//   A[t,i] = b_t rk_t rk_i (K_E K_F^T)[t,i],  M'[t,i] = rqs_t (Q_E K_F^T)[t,i]
+//   A[t,i] = b_t rk_t rk_i (X K_G^T)[t,i],  M'[t,i] = rqs_t (Q_T K_G^T)[t,i]
 //   D = V - rk (X S),  N = diag(b) D + L D,  N' = rk N
 //   O = rqs (Q_T S) + M' N',  S <- Diag(e^{G_last}) S + K'^T N'
-// with X = e^G k, Q_T = e^G q, K' = e^{G_last - G} k (raw k, q) and
-// L = ((I + A)^-1 - I) diag(b).
+// with X = e^G k, Q_T = e^G q, K_G = e^{-G} k, K' = e^{G_last - G} k (raw
+// k, q) and L = ((I + A)^-1 - I) diag(b).
 //
-// Exponent ranges.  The products A and M use a reference R = G at token 7
-// (K_E = k e^{G-R}, Q_E = q e^{G-R}, K_F = k e^{R-G}): every factor stays within
-// 2^{+-8 |lower_bound| log2 e}, far from fp32/bf16 under- and overflow, so
-// small k entries keep their relative precision.  The state-side operands use
-// the chunk start (X, Q_T <= |k|, |q|) and the chunk end (K' <= |k|); where
-// those underflow the true contribution is below 2^-126 of the state.
+// Exponent ranges.  G is taken from the chunk start, so X and Q_T are at most
+// |k|, |q| and K' at most |k|, while K_G = e^{-G} k grows up to
+// 2^{16 |lower_bound| log2 e} |k|.  With lower_bound >= kPipeLowerBoundMin
+// (-5) that is 2^115.4 |k|, inside the bf16/fp32 range; X keeps full
+// precision down to |k| ~ 2^-10 at the strongest decay.  Products of pairs
+// t < i (discarded) may overflow; they are dropped by selects, not by
+// multiplication.  Stronger lower bounds are served by the 64-token kernel.
 //
 // Precision (checked against the fp64 recurrence on the workloads'
 // distributions): bf16 MFMA operands with fp32 accumulation; the inverse by
@@ -79,12 +80,23 @@ __device__ __forceinline__ int frag(int blk, int m, int k) {
   return blk * 256 + ((k >> 2) * 16 + m) * 4 + (k & 3);
 }
 
+// Buffer resources over one head's rows of a [T, H, ...] tensor, bounded at
+// the end of the sequence: loads past it return 0 and stores past it are
+// dropped by the hardware range check, so partial chunks need no branches.
+// (gfx9 buffer descriptor word 3: 32-bit untyped data.)
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int eos, int rowstride,
+                                                          int rowlen) {
+  const int bytes = eos > 0 ? ((eos - 1) * rowstride + rowlen) * 2 : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+
 // One chunk's package: written by one producer wave, read by the state waves.
 struct Pack {
-  bf16 x[128 * kTok];    // e^{G} k, swizzled rows; scratch before that: Q_E
-  bf16 qt[128 * kTok];   // e^{G} q, swizzled rows
-  bf16 kph[128 * kTok];  // K' high part, fragment order (block = 16 keys); scratch: K_E
-  bf16 kpl[128 * kTok];  // K' low part; scratch: K_F
+  bf16 x[128 * kTok];    // X = e^{G} k, swizzled rows
+  bf16 qt[128 * kTok];   // Q_T = e^{G} q, swizzled rows
+  bf16 kph[128 * kTok];  // K' high part, fragment order (block = 16 keys); scratch: K_G
+  bf16 kpl[128 * kTok];  // K' low part
   bf16 l[256];           // L, fragment order
   bf16 m[256];           // M', fragment order
   float beta[kTok];
@@ -103,42 +115,27 @@ struct Raw {
   uint32_t beta;
 };
 
-__device__ __forceinline__ void load_raw(Raw& r, const uint16_t* qb, const uint16_t* kb,
-                                         const uint16_t* gb, const uint16_t* bb, int rowstride,
-                                         int H, int t0, int Lc, int lane) {
-  const unsigned ch = 4u * unsigned(lane >> 1);
-  const int th = lane & 1;
-  if (Lc == kTok) {
+struct RawSrc {
+  __amdgpu_buffer_rsrc_t q, k, g, beta;  // head h, bounded at the sequence end
+};
+
+// Rows past the sequence end read as zeros (buffer range check).
+__device__ __forceinline__ void load_raw(Raw& r, const RawSrc& src, int rowstride, int H, int t0,
+                                         int lane) {
+  const unsigned ch = 4u * unsigned(lane >> 1), th = unsigned(lane & 1);
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      const unsigned off = unsigned(t0 + 8 * th + rr) * unsigned(rowstride) + ch;
-      r.q[rr] = *reinterpret_cast<const uint2*>(qb + off);
-      r.k[rr] = *reinterpret_cast<const uint2*>(kb + off);
-      r.g[rr] = *reinterpret_cast<const uint2*>(gb + off);
-    }
-  } else {
-#pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      if (8 * th + rr < Lc) {
-        const unsigned off = unsigned(t0 + 8 * th + rr) * unsigned(rowstride) + ch;
-        r.q[rr] = *reinterpret_cast<const uint2*>(qb + off);
-        r.k[rr] = *reinterpret_cast<const uint2*>(kb + off);
-        r.g[rr] = *reinterpret_cast<const uint2*>(gb + off);
-      } else {
-        r.q[rr] = r.k[rr] = r.g[rr] = uint2{0u, 0u};
-      }
-    }
+  for (int rr = 0; rr < 8; ++rr) {
+    const unsigned off = ((unsigned(t0) + 8u * th + rr) * unsigned(rowstride) + ch) * 2u;
+    r.q[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.q, off, 0, 0));
+    r.k[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.k, off, 0, 0));
+    r.g[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.g, off, 0, 0));
   }
-  const int tn = lane >> 2;
-  if (tn < Lc) {
-    const unsigned off = unsigned(t0 + tn) * unsigned(rowstride) + 32u * unsigned(lane & 3);
+  const unsigned offn =
+      ((unsigned(t0) + unsigned(lane >> 2)) * unsigned(rowstride) + 32u * unsigned(lane & 3)) * 2u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.qn[i] = *reinterpret_cast<const uint4*>(qb + off + 8 * i);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.qn[i] = uint4{0u, 0u, 0u, 0u};
-  }
-  r.beta = lane < Lc ? uint32_t(bb[unsigned(t0 + lane) * unsigned(H)]) : 0u;
+  for (int i = 0; i < 4; ++i)
+    r.qn[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src.q, offn + 16u * i, 0, 0));
+  r.beta = __builtin_amdgcn_raw_buffer_load_b16(src.beta, (unsigned(t0) + unsigned(lane)) * unsigned(H) * 2u, 0, 0);
 }
 
 __device__ __forceinline__ float dot2(uint32_t a, float c) {
@@ -156,15 +153,16 @@ __device__ __forceinline__ float chan(uint2 w, int i) {
   return (i & 1) ? bf16_hi(d) : bf16_lo(d);
 }
 
-// Values a producer keeps in registers across its MFMA step: X and the two
-// parts of K', packed bf16 pairs of consecutive tokens, per channel.
+// Values a producer keeps in registers across its MFMA step: the two parts of
+// K', packed bf16 pairs of consecutive tokens, per channel.
 struct Held {
-  uint32_t x[4][4], kh[4][4], kl[4][4];
+  uint32_t kh[4][4], kl[4][4];
 };
 
 // Producer, first half: norms of q, beta, the gate and its cumulative sum,
-// and every decayed operand.  Writes Q_T, the scratch operands of the A / M
-// products, gam, beta and rqs; returns X and K' in `held`.  FULL: all 16
+// and every decayed operand.  Writes X = e^G k and Q_T = e^G q (which are
+// also the left operands of the A and M products), the scratch right operand
+// K_G = e^{-G} k, gam, beta and rqs; returns K' in `held`.  FULL: all 16
 // tokens are inside the sequence (no masking).
 template <bool FULL>
 __device__ __forceinline__ void produce_operands(Pack& pk, const Raw& raw, Held& held, int Lc,
@@ -203,68 +201,57 @@ __device__ __forceinline__ void produce_operands(Pack& pk, const Raw& raw, Held&
     }
   }
 
-  // R = G at token 7.  Lane th = 0 holds tokens 0..7 (G_t - R = lb2 (cs_t - cs_7)),
-  // lane th = 1 tokens 8..15 (G_t - R = lb2 cs_t); the partner lane supplies
-  // the other half's total.
-  float off[4], eR[4], eLR[4];
+  // G relative to the chunk start.  Lane th = 0 holds tokens 0..7, lane
+  // th = 1 tokens 8..15 and adds the partner's total of tokens 0..7.
+  float off[4], gam[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float own = cs[i][7], other = pair_swap(own);
-    const float s7 = th ? other : own;    // sigma sum of tokens 0..7
-    const float s15 = th ? own : other;   // sigma sum of tokens 8..15
-    off[i] = th ? 0.f : -lb2 * own;
-    eR[i] = ex2(lb2 * s7);                // e^{R} (chunk start to token 7)
-    eLR[i] = ex2(lb2 * s15);              // e^{G_last - R}
+    off[i] = th ? lb2 * other : 0.f;
+    gam[i] = ex2(lb2 * (own + other));  // e^{G_last}
   }
-  if (th == 0)
-    *reinterpret_cast<f32x4*>(&pk.gam[4 * cg]) =
-        f32x4{eR[0] * eLR[0], eR[1] * eLR[1], eR[2] * eLR[2], eR[3] * eLR[3]};
+  if (th == 0) *reinterpret_cast<f32x4*>(&pk.gam[4 * cg]) = f32x4{gam[0], gam[1], gam[2], gam[3]};
 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = swz(4 * cg + i) * kTok + 8 * th;  // this lane's 8 tokens of channel 4cg+i
-    uint32_t ke[4], kf[4], qe[4], qt[4];
+    uint32_t xk[4], qk[4], kg[4];
 #pragma unroll
     for (int pr = 0; pr < 4; ++pr) {
-      float vke[2], vkf[2], vqe[2], vqt[2], vx[2], vkp[2];
+      float vx[2], vq[2], vg[2], vkp[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int rr = 2 * pr + h;
-        const float x = fmaf(cs[i][rr], lb2, off[i]);  // G - R
-        const float E = ex2(x), F = ex2(-x);
+        const float G = fmaf(cs[i][rr], lb2, off[i]);
+        const float E = ex2(G), F = ex2(-G);
         const float kv = chan(raw.k[rr], i), qv = chan(raw.q[rr], i);
-        vke[h] = kv * E;
-        vkf[h] = kv * F;
-        vqe[h] = qv * E;
-        vqt[h] = vqe[h] * eR[i];
-        vx[h] = vke[h] * eR[i];
-        vkp[h] = vkf[h] * eLR[i];
+        vx[h] = kv * E;
+        vq[h] = qv * E;
+        vg[h] = kv * F;
+        vkp[h] = vg[h] * gam[i];
       }
-      ke[pr] = pk2(vke[0], vke[1]);
-      kf[pr] = pk2(vkf[0], vkf[1]);
-      qe[pr] = pk2(vqe[0], vqe[1]);
-      qt[pr] = pk2(vqt[0], vqt[1]);
-      held.x[i][pr] = pk2(vx[0], vx[1]);
+      xk[pr] = pk2(vx[0], vx[1]);
+      qk[pr] = pk2(vq[0], vq[1]);
+      kg[pr] = pk2(vg[0], vg[1]);
       const uint32_t hi = pk2(vkp[0], vkp[1]);
       held.kh[i][pr] = hi;
       held.kl[i][pr] = pk2(vkp[0] - bf16_lo(hi), vkp[1] - bf16_hi(hi));
     }
-    *reinterpret_cast<uint4*>(&pk.kph[row]) = uint4{ke[0], ke[1], ke[2], ke[3]};
-    *reinterpret_cast<uint4*>(&pk.kpl[row]) = uint4{kf[0], kf[1], kf[2], kf[3]};
-    *reinterpret_cast<uint4*>(&pk.x[row]) = uint4{qe[0], qe[1], qe[2], qe[3]};
-    *reinterpret_cast<uint4*>(&pk.qt[row]) = uint4{qt[0], qt[1], qt[2], qt[3]};
+    *reinterpret_cast<uint4*>(&pk.x[row]) = uint4{xk[0], xk[1], xk[2], xk[3]};
+    *reinterpret_cast<uint4*>(&pk.qt[row]) = uint4{qk[0], qk[1], qk[2], qk[3]};
+    *reinterpret_cast<uint4*>(&pk.kph[row]) = uint4{kg[0], kg[1], kg[2], kg[3]};
   }
 }
 
 // Producer, second half: the A and M products, 1/||k||, the inverse and L,
-// then X and K' over the scratch operands (this wave's own LDS accesses are
-// processed in order, so the scratch reads are done before they are
+// then K' over the scratch operand (this wave's own LDS accesses are
+// processed in order, so the scratch reads are done before it is
 // overwritten).
 __device__ __forceinline__ void produce_products(Pack& pk, const Held& held, int lane) {
   const int l16 = lane & 15, g4 = lane >> 4;
   const int cg = lane >> 1, th = lane & 1;
 
-  // A = K_E K_F^T, A^T = K_F K_E^T and M'^T = K_F Q_E^T over the 128 channels;
+  // A = X K_G^T, A^T = K_G X^T and M'^T = K_G Q_T^T over the 128 channels;
   // k-slots 8 g4 .. 8 g4 + 7 of each 32-channel block, on both sides
   __builtin_amdgcn_wave_barrier();  // the operands were written by other lanes of this wave
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -274,12 +261,12 @@ __device__ __forceinline__ void produce_products(Pack& pk, const Held& held, int
   for (int kb = 0; kb < 4; ++kb) {
     const int r1 = 32 * kb + 8 * g4 + (l16 >> 2), r2 = r1 + 4;
     const int o1 = swz(r1) * kTok + col, o2 = swz(r2) * kTok + col;
-    const bf16x8 KE = cat(tr4(&pk.kph[o1]), tr4(&pk.kph[o2]));
-    const bf16x8 KF = cat(tr4(&pk.kpl[o1]), tr4(&pk.kpl[o2]));
-    const bf16x8 QE = cat(tr4(&pk.x[o1]), tr4(&pk.x[o2]));
-    accA = mfma32(KE, KF, accA);     // [t = 4g4+j][i = l16]
-    accAt = mfma32(KF, KE, accAt);   // [i = 4g4+j][t = l16]
-    accMt = mfma32(KF, QE, accMt);   // [i = 4g4+j][t = l16]
+    const bf16x8 KE = cat(tr4(&pk.x[o1]), tr4(&pk.x[o2]));
+    const bf16x8 KG = cat(tr4(&pk.kph[o1]), tr4(&pk.kph[o2]));
+    const bf16x8 QE = cat(tr4(&pk.qt[o1]), tr4(&pk.qt[o2]));
+    accA = mfma32(KE, KG, accA);     // [t = 4g4+j][i = l16]
+    accAt = mfma32(KG, KE, accAt);   // [i = 4g4+j][t = l16]
+    accMt = mfma32(KG, QE, accMt);   // [i = 4g4+j][t = l16]
   }
 
   // 1/||k_t|| from the diagonal (lane l16 of group l16/4 holds element (l16, l16))
@@ -324,13 +311,11 @@ __device__ __forceinline__ void produce_products(Pack& pk, const Held& held, int
     *reinterpret_cast<bf16x4*>(&pk.l[frag(0, l16, 4 * g4)]) = to_bf16x4((Dt - I4) * bR);
   }
 
-  // X over Q_E, K' over K_E / K_F (after every lane's operand reads above)
+  // K' over K_G (this wave's scratch reads above come first in its LDS order)
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = 4 * cg + i;
-    *reinterpret_cast<uint4*>(&pk.x[swz(c) * kTok + 8 * th]) =
-        uint4{held.x[i][0], held.x[i][1], held.x[i][2], held.x[i][3]};
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int o = frag(c >> 4, c & 15, 8 * th + 4 * hh);
@@ -340,16 +325,16 @@ __device__ __forceinline__ void produce_products(Pack& pk, const Held& held, int
   }
 }
 
-// Value strip of one chunk for a state lane: tokens 4 g4 + j, one column.
-__device__ __forceinline__ uint2 load_v4(const uint16_t* vcol, int rowstride, int t0, int Lc,
-                                         int g4) {
-  uint16_t e[4];
+// Value strip of one chunk for a state lane: tokens 4 g4 + j of one column,
+// one register each, raw bf16 bits (zero past the sequence end).  Nothing
+// combines the values here, so nothing waits for these loads before the
+// chunk that uses them.
+__device__ __forceinline__ void load_v4(uint32_t* e, __amdgpu_buffer_rsrc_t v, unsigned col,
+                                        int rowstride, int t0, int g4) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = 4 * g4 + j;
-    e[j] = t < Lc ? vcol[unsigned(t0 + t) * unsigned(rowstride)] : uint16_t(0);
-  }
-  return uint2{uint32_t(e[0]) | (uint32_t(e[1]) << 16), uint32_t(e[2]) | (uint32_t(e[3]) << 16)};
+  for (int j = 0; j < 4; ++j)
+    e[j] = __builtin_amdgcn_raw_buffer_load_b16(
+        v, ((unsigned(t0) + unsigned(4 * g4 + j)) * unsigned(rowstride) + col) * 2u, 0, 0);
 }
 
 template <int VS>
@@ -383,21 +368,20 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
 
   if (wave < kPW) {
     // ---------------- producer waves ----------------
-    const uint16_t* qb = p.q + size_t(h) * kD;
-    const uint16_t* kb = p.k + size_t(h) * kD;
-    const uint16_t* gb = p.g + size_t(h) * kD;
-    const uint16_t* betab = p.beta + h;
+    RawSrc src;
+    src.q = rows_rsrc(p.q + size_t(h) * kD, eos, rowstride, kD);
+    src.k = rows_rsrc(p.k + size_t(h) * kD, eos, rowstride, kD);
+    src.g = rows_rsrc(p.g + size_t(h) * kD, eos, rowstride, kD);
+    src.beta = rows_rsrc(p.beta + h, eos, H, 1);
     const float eA = expf(p.A_log[h]);
     const float c1 = -kLog2e * eA;
     const float lb2 = p.lower_bound * kLog2e;
     float c2[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) c2[i] = c1 * p.dt_bias[h * kD + 4 * (lane >> 1) + i];
+    __builtin_amdgcn_sched_barrier(0);  // constants first: nothing waits behind the first chunk's loads
     Raw raw;
-    if (wave < nc) {
-      const int t0 = bos + kTok * wave;
-      load_raw(raw, qb, kb, gb, betab, rowstride, H, t0, min(kTok, eos - t0), lane);
-    }
+    if (wave < nc) load_raw(raw, src, rowstride, H, bos + kTok * wave, lane);
     for (int r = 0; r <= nr; ++r) {
       const int j = kPW * r + wave;
       if (r < nr && j < nc) {
@@ -408,7 +392,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
         else produce_operands<false>(P, raw, held, Lc, lane, c2, c1, lb2, p.scale);
         // this wave's next chunk, one round ahead
         const int tn = t0 + kTok * kPW;
-        if (tn < eos) load_raw(raw, qb, kb, gb, betab, rowstride, H, tn, min(kTok, eos - tn), lane);
+        if (tn < eos) load_raw(raw, src, rowstride, H, tn, lane);
         produce_products(P, held, lane);
       }
       __syncthreads();
@@ -417,113 +401,157 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   }
 
   // ---------------- state waves ----------------
+  // The state waves carry the serial chain; give them issue priority over the
+  // producer wave that shares their SIMD.
+  __builtin_amdgcn_s_setprio(2);
   // S[u][rt][j] = S[16 rt + 4 g4 + j][column of strip u]
   const int sw = wave - kPW;
   const int colb = slice * VS + 16 * sw + l16;  // column of strip 0; strip u adds 16 NSW u
-  const uint16_t* vb = p.v + size_t(h) * kD + colb;
-  uint16_t* ob = p.out + size_t(h) * kD + colb;
+  const __amdgpu_buffer_rsrc_t vsrc = rows_rsrc(p.v + size_t(h) * kD, eos, rowstride, kD);
+  const __amdgpu_buffer_rsrc_t odst = rows_rsrc(p.out + size_t(h) * kD, eos, rowstride, kD);
   const size_t sbase = (size_t(n) * H + h) * kD * kD;
   f32x4 S[SPW][8];
+  if (!p.s0) {
 #pragma unroll
-  for (int u = 0; u < SPW; ++u)
+    for (int u = 0; u < SPW; ++u)
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt) {
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (p.s0) {
+      for (int rt = 0; rt < 8; ++rt) S[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else if (p.state_bf16) {
+    const uint16_t* s0 = static_cast<const uint16_t*>(p.s0) + sbase + colb;
+    uint16_t raw0[SPW][8][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const size_t idx = sbase + size_t(16 * rt + 4 * g4 + j) * kD + colb + 16 * NSW * u;
-          x[j] = p.state_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p.s0)[idx])
-                              : static_cast<const float*>(p.s0)[idx];
-        }
-      }
-      S[u][rt] = x;
-    }
-  uint2 vnext[kPW][SPW], vcur[kPW][SPW];
+    for (int u = 0; u < SPW; ++u)
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) raw0[u][rt][j] = s0[(16 * rt + 4 * g4 + j) * kD + 16 * NSW * u];
+#pragma unroll
+    for (int u = 0; u < SPW; ++u)
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[u][rt][j] = bf16_to_f32(raw0[u][rt][j]);
+  } else {
+    const float* s0 = static_cast<const float*>(p.s0) + sbase + colb;
+#pragma unroll
+    for (int u = 0; u < SPW; ++u)
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[u][rt][j] = s0[(16 * rt + 4 * g4 + j) * kD + 16 * NSW * u];
+  }
+  // values of each round's chunks, loaded one round before use into two
+  // alternating register sets (no copies, so nothing waits for the output
+  // stores issued in between)
+  uint32_t va[kPW][SPW][4], vbuf[kPW][SPW][4];
 #pragma unroll
   for (int c = 0; c < kPW; ++c)
 #pragma unroll
-    for (int u = 0; u < SPW; ++u) vnext[c][u] = uint2{0u, 0u};
-
-  for (int r = 0; r <= nr; ++r) {
-    // values of this round's chunks (consumed next round)
+    for (int u = 0; u < SPW; ++u)
 #pragma unroll
-    for (int c = 0; c < kPW; ++c)
+      for (int j = 0; j < 4; ++j) va[c][u][j] = vbuf[c][u][j] = 0u;
+
+  auto load_round = [&](uint32_t (&v)[kPW][SPW][4], int r) {
+    if (r >= nr) return;
+#pragma unroll
+    for (int c = 0; c < kPW; ++c) {
+      const int t0 = bos + kTok * (kPW * r + c);
+      if (t0 < eos)
+#pragma unroll
+        for (int u = 0; u < SPW; ++u) load_v4(v[c][u], vsrc, colb + 16 * NSW * u, rowstride, t0, g4);
+    }
+  };
+  // the chunks of round r - 1, in order
+  auto consume_round = [&](const uint32_t (&v)[kPW][SPW][4], int r) {
+#pragma unroll
+    for (int c = 0; c < kPW; ++c) {
+      const int j = kPW * (r - 1) + c;
+      if (j >= nc) break;
+      const Pack& P = pk[(r - 1) & 1][c];
+      const int t0 = bos + kTok * j;
+
+      // X and Q_T as A operands; k-slots {32kb + 4g4 + j, 32kb + 16 + 4g4 + j}
+      // match the B operand built from two accumulator tiles of S
+      bf16x8 ax[4], aq[4];
+      const int col = 4 * (l16 & 3);
+#pragma unroll
+      for (int kb2 = 0; kb2 < 4; ++kb2) {
+        const int r1 = 32 * kb2 + 4 * g4 + (l16 >> 2), r2 = r1 + 16;
+        const int o1 = swz(r1) * kTok + col, o2 = swz(r2) * kTok + col;
+        ax[kb2] = cat(tr4(&P.x[o1]), tr4(&P.x[o2]));
+        aq[kb2] = cat(tr4(&P.qt[o1]), tr4(&P.qt[o2]));
+      }
+      const f32x4 bR = *reinterpret_cast<const f32x4*>(&P.beta[4 * g4]);
+      const f32x4 rkR = *reinterpret_cast<const f32x4*>(&P.rk[4 * g4]);
+      const f32x4 rqR = *reinterpret_cast<const f32x4*>(&P.rqs[4 * g4]);
+      const bf16x4 Lf = *reinterpret_cast<const bf16x4*>(&P.l[frag(0, l16, 4 * g4)]);
+      const bf16x4 Mf = *reinterpret_cast<const bf16x4*>(&P.m[frag(0, l16, 4 * g4)]);
+
 #pragma unroll
       for (int u = 0; u < SPW; ++u) {
-        vcur[c][u] = vnext[c][u];
-        const int t0 = bos + kTok * (kPW * r + c);
-        vnext[c][u] = r < nr && t0 < eos
-                          ? load_v4(vb + 16 * NSW * u, rowstride, t0, min(kTok, eos - t0), g4)
-                          : uint2{0u, 0u};
-      }
-    if (r >= 1) {
+        bf16x8 Sb[4];
 #pragma unroll
-      for (int c = 0; c < kPW; ++c) {
-        const int j = kPW * (r - 1) + c;
-        if (j >= nc) break;
-        const Pack& P = pk[(r - 1) & 1][c];
-        const int t0 = bos + kTok * j, Lc = min(kTok, eos - t0);
-
-        // X and Q_T as A operands; k-slots {32kb + 4g4 + j, 32kb + 16 + 4g4 + j}
-        // match the B operand built from two accumulator tiles of S
-        bf16x8 ax[4], aq[4];
-        const int col = 4 * (l16 & 3);
+        for (int kb2 = 0; kb2 < 4; ++kb2)
+          Sb[kb2] = cat(to_bf16x4(S[u][2 * kb2]), to_bf16x4(S[u][2 * kb2 + 1]));
+        f32x4 Y = {0.f, 0.f, 0.f, 0.f}, Q = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb2 = 0; kb2 < 4; ++kb2) {
-          const int r1 = 32 * kb2 + 4 * g4 + (l16 >> 2), r2 = r1 + 16;
-          const int o1 = swz(r1) * kTok + col, o2 = swz(r2) * kTok + col;
-          ax[kb2] = cat(tr4(&P.x[o1]), tr4(&P.x[o2]));
-          aq[kb2] = cat(tr4(&P.qt[o1]), tr4(&P.qt[o2]));
+          Y = mfma32(ax[kb2], Sb[kb2], Y);
+          Q = mfma32(aq[kb2], Sb[kb2], Q);
         }
-        const f32x4 bR = *reinterpret_cast<const f32x4*>(&P.beta[4 * g4]);
-        const f32x4 rkR = *reinterpret_cast<const f32x4*>(&P.rk[4 * g4]);
-        const f32x4 rqR = *reinterpret_cast<const f32x4*>(&P.rqs[4 * g4]);
-        const bf16x4 Lf = *reinterpret_cast<const bf16x4*>(&P.l[frag(0, l16, 4 * g4)]);
-        const bf16x4 Mf = *reinterpret_cast<const bf16x4*>(&P.m[frag(0, l16, 4 * g4)]);
-
+        f32x4 V;
 #pragma unroll
-        for (int u = 0; u < SPW; ++u) {
-          bf16x8 Sb[4];
+        for (int jj = 0; jj < 4; ++jj) V[jj] = bf16_lo(v[c][u][jj]);
+        const f32x4 D = V - rkR * Y;
+        const f32x4 N = mfma16(Lf, to_bf16x4(D), bR * D);
+        const f32x4 Np = rkR * N;
+        const bf16x4 Nh = to_bf16x4(Np);
+        const bf16x4 Nl = to_bf16x4(Np - to_f32x4(Nh));
+        const f32x4 O = mfma16(Mf, Nh, rqR * Q);
+        // rows past the sequence end are dropped by the range check (the
+        // halves are taken from packed words: storing bf16 vector elements
+        // directly through the 16-bit buffer store is miscompiled)
+        const uint32_t w01 = pk2(O[0], O[1]), w23 = pk2(O[2], O[3]);
+        const unsigned short ov[4] = {(unsigned short)w01, (unsigned short)(w01 >> 16),
+                                      (unsigned short)w23, (unsigned short)(w23 >> 16)};
 #pragma unroll
-          for (int kb2 = 0; kb2 < 4; ++kb2)
-            Sb[kb2] = cat(to_bf16x4(S[u][2 * kb2]), to_bf16x4(S[u][2 * kb2 + 1]));
-          f32x4 Y = {0.f, 0.f, 0.f, 0.f}, Q = {0.f, 0.f, 0.f, 0.f};
+        for (int jj = 0; jj < 4; ++jj)
+          __builtin_amdgcn_raw_buffer_store_b16(
+              ov[jj], odst,
+              ((unsigned(t0) + unsigned(4 * g4 + jj)) * unsigned(rowstride) + colb + 16 * NSW * u) * 2u,
+              0, 0);
+        // S <- Diag(e^{G_last}) S + K'^T N', two-term split on both sides:
+        // K'h N'h + K'l N'h as one 32-deep product (k-slots: this lane group's
+        // four tokens, high part then low part), then K'h N'l as a 32-deep
+        // product with a zero half.  (Both are 16x16x32: on gfx950 a 16x16x16
+        // product accumulating straight onto a 16x16x32 result was observed to
+        // return wrong sums.)
+        const bf16x8 Nhh = cat(Nh, Nh), Nl0 = cat(Nl, bf16x4{});
 #pragma unroll
-          for (int kb2 = 0; kb2 < 4; ++kb2) {
-            Y = mfma32(ax[kb2], Sb[kb2], Y);
-            Q = mfma32(aq[kb2], Sb[kb2], Q);
-          }
-          const uint2 vw = vcur[c][u];
-          const f32x4 V = {bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y)};
-          const f32x4 D = V - rkR * Y;
-          const f32x4 N = mfma16(Lf, to_bf16x4(D), bR * D);
-          const f32x4 Np = rkR * N;
-          const bf16x4 Nh = to_bf16x4(Np);
-          const bf16x4 Nl = to_bf16x4(Np - to_f32x4(Nh));
-          const f32x4 O = mfma16(Mf, Nh, rqR * Q);
-          bf16* orow = reinterpret_cast<bf16*>(ob) + 16 * NSW * u;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int t = 4 * g4 + jj;
-            if (t < Lc) orow[unsigned(t0 + t) * unsigned(rowstride)] = (bf16)O[jj];
-          }
-          // S <- Diag(e^{G_last}) S + K'^T N', two-term split on both sides
-#pragma unroll
-          for (int rt = 0; rt < 8; ++rt) {
-            const f32x4 gm = *reinterpret_cast<const f32x4*>(&P.gam[16 * rt + 4 * g4]);
-            const bf16x4 ah = *reinterpret_cast<const bf16x4*>(&P.kph[frag(rt, l16, 4 * g4)]);
-            const bf16x4 al = *reinterpret_cast<const bf16x4*>(&P.kpl[frag(rt, l16, 4 * g4)]);
-            f32x4 s = S[u][rt] * gm;
-            s = mfma16(ah, Nh, s);
-            s = mfma16(ah, Nl, s);
-            s = mfma16(al, Nh, s);
-            S[u][rt] = s;
-          }
+        for (int rt = 0; rt < 8; ++rt) {
+          const f32x4 gm = *reinterpret_cast<const f32x4*>(&P.gam[16 * rt + 4 * g4]);
+          const bf16x4 ah = *reinterpret_cast<const bf16x4*>(&P.kph[frag(rt, l16, 4 * g4)]);
+          const bf16x4 al = *reinterpret_cast<const bf16x4*>(&P.kpl[frag(rt, l16, 4 * g4)]);
+          f32x4 s = S[u][rt] * gm;
+          s = mfma32(cat(ah, al), Nhh, s);
+          s = mfma32(cat(ah, bf16x4{}), Nl0, s);
+          S[u][rt] = s;
         }
       }
     }
+  };
+
+  load_round(va, 0);
+  __syncthreads();
+  for (int r = 1; r <= nr; r += 2) {
+    load_round(vbuf, r);
+    consume_round(va, r);
     __syncthreads();
+    if (r + 1 <= nr) {
+      load_round(va, r + 1);
+      consume_round(vbuf, r + 1);
+      __syncthreads();
+    }
   }
 
   // final state

@@ -128,12 +128,14 @@ const char* kda_last_hip_error(void);
 int kda_debug_set_vsplit(int s);
 
 /*
- * Test hook: choose the kernel family -- 0: the pipelined 16-token chunk
- * kernel (the default); 1: the 64-token chunk kernel (WY/UT with a blocked
- * forward substitution over the 64x64 triangle); 2: the token-serial fp32
- * kernel, an independent GPU implementation of the same recurrence used to
- * cross-check the chunked ones.  Process-wide.  Returns the previous setting,
- * or -1 (unchanged) for an invalid value.
+ * Test hook: choose the kernel family -- 0 (default): the pipelined 16-token
+ * chunk kernel for lower_bound >= -5 with the value dimension split at least
+ * in two (a forced split of 1 and lower_bound < -5 use the 64-token kernel);
+ * 1: the 64-token chunk kernel (WY/UT with a blocked forward substitution
+ * over the 64x64 triangle); 2: the token-serial fp32 kernel, an independent
+ * GPU implementation of the same recurrence used to cross-check the chunked
+ * ones.  Process-wide.  Returns the previous setting, or -1 (unchanged) for
+ * an invalid value.
  */
 int kda_debug_set_kernel(int k);
 

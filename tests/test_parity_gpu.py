@@ -42,21 +42,56 @@ def test_config_parity(idx):
     assert_parity(x, out, fin, oref, fref, label=f"config {idx}")
 
 
+@pytest.mark.parametrize("kernel,splits", [(0, (2, 4, 8)), (1, (1, 2, 4, 8))])
 @pytest.mark.parametrize("idx", [3, 0, 1])
-def test_vsplit_bit_identical(idx):
+def test_vsplit_bit_identical(idx, kernel, splits):
+    """Splitting the value dimension over workgroups changes nothing, bit for
+    bit: each value column's arithmetic is the same whatever the split.  The
+    pipelined kernel (0) takes splits of 2 and more; the 64-token kernel (1)
+    also runs unsplit."""
     import torch
     import gated_delta_rule_tok_amd as kda
     x, _ = _config(idx)
     d = to_device(x)
     res = {}
-    for s in (1, 2, 4, 8):
-        kda.kda_debug_set_vsplit(s)
-        o, f = run_gpu(x, d)
-        torch.cuda.synchronize()
-        res[s] = (o.view(torch.int16).cpu(), f.cpu())
-    for s in (2, 4, 8):
-        assert torch.equal(res[s][0], res[1][0]), f"out differs with split {s}"
-        assert torch.equal(res[s][1], res[1][1]), f"final state differs with split {s}"
+    prev = kda.kda_debug_set_kernel(kernel)
+    try:
+        for s in splits:
+            kda.kda_debug_set_vsplit(s)
+            o, f = run_gpu(x, d)
+            torch.cuda.synchronize()
+            res[s] = (o.view(torch.int16).cpu(), f.cpu())
+    finally:
+        kda.kda_debug_set_kernel(prev)
+    s0 = splits[0]
+    for s in splits[1:]:
+        assert torch.equal(res[s][0], res[s0][0]), f"out differs with split {s}"
+        assert torch.equal(res[s][1], res[s0][1]), f"final state differs with split {s}"
+
+
+@pytest.mark.parametrize("idx", [0, 1, 3])
+def test_chunk64_kernel_parity(idx):
+    """The 64-token chunk kernel (used for lower_bound < -5 and unsplit
+    launches) matches the oracle on the workloads too."""
+    import gated_delta_rule_tok_amd as kda
+    x, (oref, fref) = _config(idx)
+    d = to_device(x)
+    prev = kda.kda_debug_set_kernel(1)
+    try:
+        out, fin = run_gpu(x, d)
+    finally:
+        kda.kda_debug_set_kernel(prev)
+    assert_parity(x, out, fin, oref, fref, label=f"64-token config {idx}")
+
+
+def test_forced_unsplit_launch():
+    """A forced split of 1 runs the 64-token kernel; results stay in parity."""
+    import gated_delta_rule_tok_amd as kda
+    x, (oref, fref) = _config(3)
+    d = to_device(x)
+    kda.kda_debug_set_vsplit(1)
+    out, fin = run_gpu(x, d)
+    assert_parity(x, out, fin, oref, fref, label="forced split 1")
 
 
 def test_repeat_calls_bit_identical():
@@ -122,13 +157,27 @@ def test_zero_tokens_keeps_state(state):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("lb", [-1.0, -5.5])
+@pytest.mark.parametrize("lb", [-1.0, -5.0, -5.5])
 def test_lower_bound_range(lb):
     x = KI.make_inputs([150, 66], 2, seed=35, init_state="fp32", lower_bound=lb)
     d = to_device(x)
     out, fin = run_gpu(x, d)
     oref, fref = run_oracle(x)
     assert_parity(x, out, fin, oref, fref, label=f"lb={lb}")
+
+
+@pytest.mark.parametrize("lb", [-5.0, -5.5])
+def test_saturated_gate(lb):
+    """dt_bias = 8 drives every gate sigmoid to ~1, so each 16-token chunk decays
+    by ~16 |lower_bound| log2(e) in log2 units: the widest exponent range the
+    kernels' decayed operands see (lower_bound -5 on the pipelined kernel, -5.5
+    on the 64-token kernel)."""
+    x = KI.make_inputs([150, 66], 2, seed=36, init_state="fp32", lower_bound=lb)
+    x.dt_bias[:] = 8.0
+    d = to_device(x)
+    out, fin = run_gpu(x, d)
+    oref, fref = run_oracle(x)
+    assert_parity(x, out, fin, oref, fref, label=f"saturated gate lb={lb}")
 
 
 @pytest.mark.parametrize("lb", [0.0, -0.05])
