@@ -56,8 +56,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+KERNEL = "pipe_kernel"  # the dominant kernel of a call (the 16-token pipelined forward)
+
+
 def traffic_file(workload: str) -> str:
-    return os.path.join(PROFILES, f"traffic__chunk_kernel__{workload}.json")
+    return os.path.join(PROFILES, f"traffic__{KERNEL}__{workload}.json")
 
 
 def _pmc_sum(path: str, kernel_sub: str):
@@ -74,11 +77,11 @@ def _pmc_sum(path: str, kernel_sub: str):
 def traffic_from_pmc(pmc_dir: str, workload: str, command: str) -> dict:
     """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) of the
     benchmark and of a plain device copy of known size into HBM bytes per
-    launch of the chunk kernel.  Expects pmc_dir/{fetch,write,cal_fetch,cal_write}/
+    launch of the dominant kernel.  Expects pmc_dir/{fetch,write,cal_fetch,cal_write}/
     run_counter_collection.csv; the calibration copy moves 256 MiB."""
     f = lambda d: os.path.join(pmc_dir, d, "run_counter_collection.csv")
-    fetch, nf = _pmc_sum(f("fetch"), "chunk_kernel")
-    write, nw = _pmc_sum(f("write"), "chunk_kernel")
+    fetch, nf = _pmc_sum(f("fetch"), KERNEL)
+    write, nw = _pmc_sum(f("write"), KERNEL)
     cal_f, _ = _pmc_sum(f("cal_fetch"), "copyBuffer")
     cal_w, _ = _pmc_sum(f("cal_write"), "copyBuffer")
     copy_kib = 256 * 1024

@@ -153,13 +153,19 @@ kda_status_t kda_chunk_prefill_fwd(const void* q, const void* k, const void* v, 
   p.state_bf16 = state_dtype == KDA_STATE_BF16;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (hipError_t e = kda::launch_plan(p, st); e != hipSuccess) return hip_failure(e, "plan launch");
   // the pipelined kernel takes lower_bound >= -5 and slices of <= 64 value
   // columns; anything else (or the test override) goes to the 64-token kernel
   int kernel = g_kernel_override.load(std::memory_order_relaxed);
   if (kernel == 0 && lower_bound < kda::kPipeLowerBoundMin) kernel = 1;
   if (kernel == 0 && p.vsplit == 1) p.vsplit = forced > 0 ? 1 : 2;
   if (kernel == 0 && p.vsplit == 1) kernel = 1;
+  // the sequence order table (longest first): the pipelined kernel ranks a
+  // few sequences itself, everything else reads the table
+  if (kernel == 0 && num_seqs <= kda::kInlineRankMax) {
+    p.order = nullptr;
+  } else if (hipError_t e = kda::launch_plan(p, st); e != hipSuccess) {
+    return hip_failure(e, "plan launch");
+  }
   if (kernel == 2) {
     if (hipError_t e = kda::launch_recurrent(p, st); e != hipSuccess)
       return hip_failure(e, "token-serial kernel launch");

@@ -25,7 +25,8 @@ struct Params {
   void* sT;
   uint16_t* out;
   const int32_t* cu;
-  int32_t* order;  // sequence processing order (longest first), [N], in the workspace
+  int32_t* order;  // sequence processing order (longest first), [N], in the workspace;
+                   // null: the kernel ranks the sequences itself (pipelined kernel, N small)
   float lower_bound;
   float scale;
   int T;           // tokens in q/k/v/g/out (sequence offsets are clamped to it)
@@ -69,7 +70,10 @@ hipError_t launch_chunk(const Params& p, hipStream_t stream);
 // state-independent operands ahead of the state waves, one workgroup per
 // (sequence, head, V-slice).  Requires lower_bound >= kPipeLowerBoundMin and a
 // value slice of at most 64 columns (vsplit >= 2).
+// With at most kInlineRankMax sequences it ranks them itself (p.order may be
+// null and no plan launch is needed).
 constexpr float kPipeLowerBoundMin = -5.0f;
+constexpr int kInlineRankMax = 16;
 hipError_t launch_pipe(const Params& p, hipStream_t stream);
 
 }  // namespace kda

@@ -104,6 +104,7 @@ struct Pack {
   float rqs[kTok];       // scale / ||q_t||
   float gam[128];        // e^{G_last}
 };
+static_assert(sizeof(Pack::gam) >= sizeof(int) * (kInlineRankMax + 1), "rank scratch fits in gam");
 
 // Raw inputs of one chunk for one producer lane: tokens 8 th + rr of channels
 // 4 cg .. 4 cg + 3 (cg = lane / 2, th = lane % 2); q again as rows for the
@@ -357,8 +358,33 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   const int slice = b % p.vsplit;
   const int rest = b / p.vsplit;
   const int h = rest % p.H;
-  const int n = p.order[rest / p.H];
   const int H = p.H;
+  // sequence of rank rest / H (longest first, ties by index): from the plan
+  // table, or ranked here when there are few sequences
+  int n;
+  if (p.order) {
+    n = p.order[rest / H];
+  } else {
+    // scratch in a package that nothing uses yet (no other LDS allocation, so
+    // the packages keep their alignment)
+    int* seq_sh = reinterpret_cast<int*>(pk[1][kPW - 1].gam);
+    const int N = p.N, target = rest / H;
+    if (tid <= N) seq_sh[tid] = p.cu[tid];
+    __syncthreads();
+    int len = 0, rank = 0;
+    if (tid < N) {
+      len = seq_sh[tid + 1] - seq_sh[tid];
+      for (int m = 0; m < N; ++m) {
+        const int lm = seq_sh[m + 1] - seq_sh[m];
+        rank += (lm > len) || (lm == len && m < tid);
+      }
+    }
+    __syncthreads();
+    if (tid < N && rank == target) seq_sh[0] = tid;
+    __syncthreads();
+    n = seq_sh[0];
+  }
+
 
   const int bos = min(max(p.cu[n], 0), p.T);
   const int eos = min(max(p.cu[n + 1], bos), p.T);
