@@ -107,14 +107,29 @@ def main():
     ap.add_argument("--sets", type=int, default=2, help="buffer sets rotated across steps")
     ap.add_argument("--traffic-from", metavar="PMC_DIR",
                     help="write the traffic file for --config from rocprofv3 counter runs, then exit")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 256 MiB device copy three times (the counter calibration), then exit")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        n = 256 * 1024 * 1024 // 4
+        a = torch.ones(n, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"copied {4 * n} bytes x3")
+        return
 
     if args.traffic_from:
         import kda_inputs as KI
         wl = KI.CONFIGS[args.config]["name"]
-        cmd = ("for c in FETCH_SIZE WRITE_SIZE: rocprofv3 --pmc $c --output-format csv -- "
-               f"python bench.py --config {args.config} --steps 3 --warmup 1 --no-cpu; the same "
-               "counters over a 256 MiB device copy for calibration")
+        cmd = ("cd /tmp && export TMPDIR=/tmp; for c in FETCH_SIZE WRITE_SIZE: rocprofv3 --pmc $c "
+               "--output-format csv -d <pmc>/<fetch|write> -o run -- python bench.py --config "
+               f"{args.config} --steps 3 --warmup 1 --no-cpu; rocprofv3 --pmc $c --output-format csv "
+               "-d <pmc>/<cal_fetch|cal_write> -o run -- python bench.py --copy-calibration; "
+               f"python bench.py --config {args.config} --traffic-from <pmc>")
         t = traffic_from_pmc(args.traffic_from, wl, cmd)
         os.makedirs(PROFILES, exist_ok=True)
         with open(traffic_file(wl), "w") as fh:

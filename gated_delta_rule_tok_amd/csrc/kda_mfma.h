@@ -1,6 +1,6 @@
-// kda_mfma.h -- gfx950 device helpers shared by the MFMA kernels: bf16 vector
-// types, the two bf16 MFMA shapes, exp2 / reciprocal, bf16 packing and the
-// transposed LDS read.
+// kda_mfma.h -- gfx950 device helpers shared by the MFMA kernels: bf16 / fp16
+// vector types, the bf16 and fp16 MFMA shapes, exp2 / reciprocal, bf16 packing
+// and the transposed LDS read.
 //
 // gfx950 facts these helpers rely on (each checked on the device):
 //  * v_mfma_f32_16x16x{32,16}_bf16: lane l holds accumulator rows 4*(l/16)+j of
@@ -13,7 +13,7 @@
 //    pointing at row base+L/4, columns c0+4*(L%4).., lane i gets column c0+i
 //    of rows base..base+3: an operand with k running over rows, read straight
 //    from a row-major array.
-//  * v_cvt_pk_bf16_f32 rounds to nearest even.
+//  * v_cvt_pk_bf16_f32 and v_cvt_pk_f16_f32 round to nearest even.
 #pragma once
 
 #include "kda_internal.h"
@@ -26,6 +26,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -35,6 +37,10 @@ static __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
 static __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+// fp16 operands (v_mfma_f32_16x16x16_f16): same lane layout as the bf16 x16 shape
+static __device__ __forceinline__ f32x4 mfma16h(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 static __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 static __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }

@@ -26,30 +26,30 @@
 // read round r-1; one workgroup barrier ends each round.  On gfx950 this puts
 // a VALU-heavy producer wave and an MFMA-heavy state wave on every SIMD.
 //
-// Norms are applied after the products, as row/column scalings: k and q enter
-// the MFMAs raw; 1/||k_t|| is read off the diagonal of the A product
-// (sum_c k_t[c] e^{x} k_t[c] e^{-x}), scale/||q_t|| comes from a separate
-// pass over q.  With rk = 1/||k|| and rqs = scale/||q||:
-//   A[t,i] = b_t rk_t rk_i (X K_G^T)[t,i],  M'[t,i] = rqs_t (Q_T K_G^T)[t,i]
-//   D = V - rk (X S),  N = diag(b) D + L D,  N' = rk N
-//   O = rqs (Q_T S) + M' N',  S <- Diag(e^{G_last}) S + K'^T N'
-// with X = e^G k, Q_T = e^G q, K_G = e^{-G} k, K' = e^{G_last - G} k (raw
-// k, q) and L = ((I + A)^-1 - I) diag(b).
+// Norms.  k is normalised before it enters any product (k~ = k / ||k||, the
+// norm from a dot-product pass over the row); q's norm is applied after the
+// products, as a row scaling.  With rqs = scale / ||q||:
+//   A[t,i] = b_t (X K_G^T)[t,i],  M'[t,i] = rqs_t (Q_T K_G^T)[t,i]
+//   D = V - X S,  N = diag(b) D + L D
+//   O = rqs (Q_T S) + M' N,  S <- Diag(e^{G_last}) S + K'^T N
+// with X = e^G k~, Q_T = e^G q, K_G = e^{-G} k~, K' = e^{G_last - G} k~ and
+// L = ((I + A)^-1 - I) diag(b).
 //
-// Exponent ranges.  G is taken from the chunk start, so X and Q_T are at most
-// |k|, |q| and K' at most |k|, while K_G = e^{-G} k grows up to
-// 2^{16 |lower_bound| log2 e} |k|.  With lower_bound >= kPipeLowerBoundMin
-// (-5) that is 2^115.4 |k|, inside the bf16/fp32 range; X keeps full
-// precision down to |k| ~ 2^-10 at the strongest decay.  Products of pairs
-// t < i (discarded) may overflow; they are dropped by selects, not by
+// Exponent ranges.  G is taken from the chunk start, so X and K' are at most
+// 1 and Q_T at most |q|, while K_G = e^{-G} k~ grows up to
+// 2^{16 |lower_bound| log2 e}.  With lower_bound >= kPipeLowerBoundMin (-5)
+// that is 2^115.4, inside the bf16/fp32 range.  Products of pairs t < i
+// (discarded) may overflow; they are dropped by selects, not by
 // multiplication.  Stronger lower bounds are served by the 64-token kernel.
 //
 // Precision (checked against the fp64 recurrence on the workloads'
 // distributions): bf16 MFMA operands with fp32 accumulation; the inverse by
 // MFMA doubling on the 16x16 block; the unit diagonal of (I + A)^-1 diag(b)
-// applied in fp32; the state update with a two-term (hi + lo) bf16 split of
-// both operands (three products), so the fp32 state does not pick up bf16
-// rounding each chunk.
+// applied in fp32.  The state update K'^T N takes fp16 operands: 16 K' (at
+// most 16) and N / 16 (both scalings exact), so |N| up to 2^20 stays inside
+// fp16's range, values below 2^-10 lose relative precision only down to an
+// absolute 2^-21 |K'| per term, and fp16's 11-bit significand keeps each
+// chunk's rounding of the fp32 state near 2^-12 of the update.
 #include "kda_mfma.h"
 
 namespace kda {
@@ -57,6 +57,8 @@ namespace {
 
 constexpr int kTok = 16;  // tokens per chunk
 constexpr int kPW = 4;    // producer waves = chunks per round
+constexpr float kKpScale = 16.f;     // K' enters the fp16 state update times this
+constexpr float kNScale = 0.0625f;   // ... and N times this (exact inverse)
 
 template <int VS>
 struct Cfg {
@@ -91,28 +93,33 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
 }
 
+template <int B>
+struct BufIdx {
+  static constexpr int value = B;
+};
+
 // One chunk's package: written by one producer wave, read by the state waves.
 struct Pack {
-  bf16 x[128 * kTok];    // X = e^{G} k, swizzled rows
+  bf16 x[128 * kTok];    // X = e^{G} k~, swizzled rows
   bf16 qt[128 * kTok];   // Q_T = e^{G} q, swizzled rows
-  bf16 kph[128 * kTok];  // K' high part, fragment order (block = 16 keys); scratch: K_G
-  bf16 kpl[128 * kTok];  // K' low part
+  bf16 kp[128 * kTok];   // kKpScale K' as fp16, fragment order (block = 16 keys);
+                         // before that, scratch for K_G (bf16, swizzled rows)
   bf16 l[256];           // L, fragment order
   bf16 m[256];           // M', fragment order
   float beta[kTok];
-  float rk[kTok];        // 1 / ||k_t||
+  float rk[kTok];        // 1 / ||k_t|| (producer scratch)
   float rqs[kTok];       // scale / ||q_t||
   float gam[128];        // e^{G_last}
 };
 static_assert(sizeof(Pack::gam) >= sizeof(int) * (kInlineRankMax + 1), "rank scratch fits in gam");
 
 // Raw inputs of one chunk for one producer lane: tokens 8 th + rr of channels
-// 4 cg .. 4 cg + 3 (cg = lane / 2, th = lane % 2); q again as rows for the
-// norm (token lane / 4, channels 32 (lane % 4) ..); the beta logit of token
-// `lane` (lanes < 16).
+// 4 cg .. 4 cg + 3 (cg = lane / 2, th = lane % 2); q and k again as rows for
+// the norms (token lane / 4, channels 32 (lane % 4) ..); the beta logit of
+// token `lane` (lanes < 16).
 struct Raw {
   uint2 q[8], k[8], g[8];
-  uint4 qn[4];
+  uint4 qn[4], kn[4];
   uint32_t beta;
 };
 
@@ -134,8 +141,10 @@ __device__ __forceinline__ void load_raw(Raw& r, const RawSrc& src, int rowstrid
   const unsigned offn =
       ((unsigned(t0) + unsigned(lane >> 2)) * unsigned(rowstride) + 32u * unsigned(lane & 3)) * 2u;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
     r.qn[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src.q, offn + 16u * i, 0, 0));
+    r.kn[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src.k, offn + 16u * i, 0, 0));
+  }
   r.beta = __builtin_amdgcn_raw_buffer_load_b16(src.beta, (unsigned(t0) + unsigned(lane)) * unsigned(H) * 2u, 0, 0);
 }
 
@@ -148,42 +157,61 @@ __device__ __forceinline__ uint32_t pk2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, bf16x2{(bf16)lo, (bf16)hi});
 }
 
+__device__ __forceinline__ uint32_t pk2h(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, f16x2{(_Float16)lo, (_Float16)hi});
+}
+
+// Sum over the four lanes 4 i .. 4 i + 3.
+__device__ __forceinline__ float quad_sum(float s) {
+  s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0xB1, 0xF, 0xF, false));
+  s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x4E, 0xF, 0xF, false));
+  return s;
+}
+
 // Channel i (0..3) of a 4-channel bf16 group.
 __device__ __forceinline__ float chan(uint2 w, int i) {
   const uint32_t d = i < 2 ? w.x : w.y;
   return (i & 1) ? bf16_hi(d) : bf16_lo(d);
 }
 
-// Values a producer keeps in registers across its MFMA step: the two parts of
-// K', packed bf16 pairs of consecutive tokens, per channel.
+// Values a producer keeps in registers across its MFMA step: kKpScale K' as
+// packed fp16 pairs of consecutive tokens, per channel.
 struct Held {
-  uint32_t kh[4][4], kl[4][4];
+  uint32_t kp[4][4];
 };
 
-// Producer, first half: norms of q, beta, the gate and its cumulative sum,
-// and every decayed operand.  Writes X = e^G k and Q_T = e^G q (which are
-// also the left operands of the A and M products), the scratch right operand
-// K_G = e^{-G} k, gam, beta and rqs; returns K' in `held`.  FULL: all 16
-// tokens are inside the sequence (no masking).
+// Producer, first half: norms of q and k, beta, the gate and its cumulative
+// sum, and every decayed operand.  Writes X = e^G k~ and Q_T = e^G q (which
+// are also the left operands of the A and M products), the scratch right
+// operand K_G = e^{-G} k~, gam, beta and rqs; returns K' in `held`.  FULL:
+// all 16 tokens are inside the sequence (no masking).
 template <bool FULL>
 __device__ __forceinline__ void produce_operands(Pack& pk, const Raw& raw, Held& held, int Lc,
                                                  int lane, const float* c2, float c1, float lb2,
                                                  float scale) {
   const int cg = lane >> 1, th = lane & 1;
 
-  // scale / ||q_t|| for token lane/4: four lanes hold 32 channels each
+  // scale / ||q_t|| and 1 / ||k_t|| for token lane/4: four lanes hold 32
+  // channels each
   {
-    float s = 0.f;
+    float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s = dot2(raw.qn[i].x, s);
-      s = dot2(raw.qn[i].y, s);
-      s = dot2(raw.qn[i].z, s);
-      s = dot2(raw.qn[i].w, s);
+      sq = dot2(raw.qn[i].x, sq);
+      sq = dot2(raw.qn[i].y, sq);
+      sq = dot2(raw.qn[i].z, sq);
+      sq = dot2(raw.qn[i].w, sq);
+      sk = dot2(raw.kn[i].x, sk);
+      sk = dot2(raw.kn[i].y, sk);
+      sk = dot2(raw.kn[i].z, sk);
+      sk = dot2(raw.kn[i].w, sk);
     }
-    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0xB1, 0xF, 0xF, false));
-    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x4E, 0xF, 0xF, false));
-    if ((lane & 3) == 0) pk.rqs[lane >> 2] = rsqrtf(s + kNormEps) * scale;
+    sq = quad_sum(sq);
+    sk = quad_sum(sk);
+    if ((lane & 3) == 0) {
+      pk.rqs[lane >> 2] = rsqrtf(sq + kNormEps) * scale;
+      pk.rk[lane >> 2] = rsqrtf(sk + kNormEps);
+    }
     if (lane < kTok)
       pk.beta[lane] = lane < Lc ? rcp(1.f + ex2(-kLog2e * bf16_to_f32(uint16_t(raw.beta)))) : 0.f;
   }
@@ -213,9 +241,15 @@ __device__ __forceinline__ void produce_operands(Pack& pk, const Raw& raw, Held&
   }
   if (th == 0) *reinterpret_cast<f32x4*>(&pk.gam[4 * cg]) = f32x4{gam[0], gam[1], gam[2], gam[3]};
 
+  // 1 / ||k|| of this lane's 8 tokens (written above by other lanes of this wave)
+  __builtin_amdgcn_wave_barrier();
+  const f32x4 rk0 = *reinterpret_cast<const f32x4*>(&pk.rk[8 * th]);
+  const f32x4 rk1 = *reinterpret_cast<const f32x4*>(&pk.rk[8 * th + 4]);
+
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = swz(4 * cg + i) * kTok + 8 * th;  // this lane's 8 tokens of channel 4cg+i
+    const float g16 = kKpScale * gam[i];
     uint32_t xk[4], qk[4], kg[4];
 #pragma unroll
     for (int pr = 0; pr < 4; ++pr) {
@@ -225,27 +259,26 @@ __device__ __forceinline__ void produce_operands(Pack& pk, const Raw& raw, Held&
         const int rr = 2 * pr + h;
         const float G = fmaf(cs[i][rr], lb2, off[i]);
         const float E = ex2(G), F = ex2(-G);
-        const float kv = chan(raw.k[rr], i), qv = chan(raw.q[rr], i);
+        const float kv = chan(raw.k[rr], i) * (rr < 4 ? rk0[rr] : rk1[rr - 4]);
+        const float qv = chan(raw.q[rr], i);
         vx[h] = kv * E;
         vq[h] = qv * E;
         vg[h] = kv * F;
-        vkp[h] = vg[h] * gam[i];
+        vkp[h] = vg[h] * g16;
       }
       xk[pr] = pk2(vx[0], vx[1]);
       qk[pr] = pk2(vq[0], vq[1]);
       kg[pr] = pk2(vg[0], vg[1]);
-      const uint32_t hi = pk2(vkp[0], vkp[1]);
-      held.kh[i][pr] = hi;
-      held.kl[i][pr] = pk2(vkp[0] - bf16_lo(hi), vkp[1] - bf16_hi(hi));
+      held.kp[i][pr] = pk2h(vkp[0], vkp[1]);
     }
     *reinterpret_cast<uint4*>(&pk.x[row]) = uint4{xk[0], xk[1], xk[2], xk[3]};
     *reinterpret_cast<uint4*>(&pk.qt[row]) = uint4{qk[0], qk[1], qk[2], qk[3]};
-    *reinterpret_cast<uint4*>(&pk.kph[row]) = uint4{kg[0], kg[1], kg[2], kg[3]};
+    *reinterpret_cast<uint4*>(&pk.kp[row]) = uint4{kg[0], kg[1], kg[2], kg[3]};
   }
 }
 
-// Producer, second half: the A and M products, 1/||k||, the inverse and L,
-// then K' over the scratch operand (this wave's own LDS accesses are
+// Producer, second half: the A and M products, the inverse and L, then K'
+// over the scratch operand (this wave's own LDS accesses are
 // processed in order, so the scratch reads are done before it is
 // overwritten).
 __device__ __forceinline__ void produce_products(Pack& pk, const Held& held, int lane) {
@@ -263,30 +296,24 @@ __device__ __forceinline__ void produce_products(Pack& pk, const Held& held, int
     const int r1 = 32 * kb + 8 * g4 + (l16 >> 2), r2 = r1 + 4;
     const int o1 = swz(r1) * kTok + col, o2 = swz(r2) * kTok + col;
     const bf16x8 KE = cat(tr4(&pk.x[o1]), tr4(&pk.x[o2]));
-    const bf16x8 KG = cat(tr4(&pk.kph[o1]), tr4(&pk.kph[o2]));
+    const bf16x8 KG = cat(tr4(&pk.kp[o1]), tr4(&pk.kp[o2]));
     const bf16x8 QE = cat(tr4(&pk.qt[o1]), tr4(&pk.qt[o2]));
     accA = mfma32(KE, KG, accA);     // [t = 4g4+j][i = l16]
     accAt = mfma32(KG, KE, accAt);   // [i = 4g4+j][t = l16]
     accMt = mfma32(KG, QE, accMt);   // [i = 4g4+j][t = l16]
   }
 
-  // 1/||k_t|| from the diagonal (lane l16 of group l16/4 holds element (l16, l16))
-  {
-    const int jd = l16 & 3;
-    const float dg = jd == 0 ? accA[0] : jd == 1 ? accA[1] : jd == 2 ? accA[2] : accA[3];
-    if (g4 == (l16 >> 2)) pk.rk[l16] = rsqrtf(dg + kNormEps);
-  }
-  __builtin_amdgcn_wave_barrier();  // rk, beta, rqs were written by other lanes of this wave
+  // beta and rqs were written by other lanes of this wave (before the
+  // operand writes that the barrier above orders)
   const f32x4 bR = *reinterpret_cast<const f32x4*>(&pk.beta[4 * g4]);
-  const f32x4 rkR = *reinterpret_cast<const f32x4*>(&pk.rk[4 * g4]);
-  const float bC = pk.beta[l16], rkC = pk.rk[l16], rqC = pk.rqs[l16];
+  const float bC = pk.beta[l16], rqC = pk.rqs[l16];
 
   f32x4 Nn, Nt, Mv, I4;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 4 * g4 + j;
-    Nn[j] = l16 < r ? bR[j] * rkR[j] * rkC * accA[j] : 0.f;    // A[r][l16]
-    Nt[j] = r < l16 ? bC * rkC * rkR[j] * accAt[j] : 0.f;      // A[l16][r]
+    Nn[j] = l16 < r ? bR[j] * accA[j] : 0.f;    // A[r][l16]
+    Nt[j] = r < l16 ? bC * accAt[j] : 0.f;      // A[l16][r]
     Mv[j] = r <= l16 ? rqC * accMt[j] : 0.f;                   // M'[l16][r]
     I4[j] = r == l16 ? 1.f : 0.f;
   }
@@ -320,8 +347,7 @@ __device__ __forceinline__ void produce_products(Pack& pk, const Held& held, int
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int o = frag(c >> 4, c & 15, 8 * th + 4 * hh);
-      *reinterpret_cast<uint2*>(&pk.kph[o]) = uint2{held.kh[i][2 * hh], held.kh[i][2 * hh + 1]};
-      *reinterpret_cast<uint2*>(&pk.kpl[o]) = uint2{held.kl[i][2 * hh], held.kl[i][2 * hh + 1]};
+      *reinterpret_cast<uint2*>(&pk.kp[o]) = uint2{held.kp[i][2 * hh], held.kp[i][2 * hh + 1]};
     }
   }
 }
@@ -487,13 +513,15 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
         for (int u = 0; u < SPW; ++u) load_v4(v[c][u], vsrc, colb + 16 * NSW * u, rowstride, t0, g4);
     }
   };
-  // the chunks of round r - 1, in order
-  auto consume_round = [&](const uint32_t (&v)[kPW][SPW][4], int r) {
+  // the chunks of round r - 1, in order, from package buffer B = (r - 1) % 2
+  // (a compile-time index, so every LDS read is a lane offset plus a constant)
+  auto consume_round = [&](const uint32_t (&v)[kPW][SPW][4], int r, auto buf) {
+    constexpr int B = decltype(buf)::value;
 #pragma unroll
     for (int c = 0; c < kPW; ++c) {
       const int j = kPW * (r - 1) + c;
       if (j >= nc) break;
-      const Pack& P = pk[(r - 1) & 1][c];
+      const Pack& P = pk[B][c];
       const int t0 = bos + kTok * j;
 
       // X and Q_T as A operands; k-slots {32kb + 4g4 + j, 32kb + 16 + 4g4 + j}
@@ -508,7 +536,6 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
         aq[kb2] = cat(tr4(&P.qt[o1]), tr4(&P.qt[o2]));
       }
       const f32x4 bR = *reinterpret_cast<const f32x4*>(&P.beta[4 * g4]);
-      const f32x4 rkR = *reinterpret_cast<const f32x4*>(&P.rk[4 * g4]);
       const f32x4 rqR = *reinterpret_cast<const f32x4*>(&P.rqs[4 * g4]);
       const bf16x4 Lf = *reinterpret_cast<const bf16x4*>(&P.l[frag(0, l16, 4 * g4)]);
       const bf16x4 Mf = *reinterpret_cast<const bf16x4*>(&P.m[frag(0, l16, 4 * g4)]);
@@ -528,12 +555,9 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
         f32x4 V;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) V[jj] = bf16_lo(v[c][u][jj]);
-        const f32x4 D = V - rkR * Y;
+        const f32x4 D = V - Y;
         const f32x4 N = mfma16(Lf, to_bf16x4(D), bR * D);
-        const f32x4 Np = rkR * N;
-        const bf16x4 Nh = to_bf16x4(Np);
-        const bf16x4 Nl = to_bf16x4(Np - to_f32x4(Nh));
-        const f32x4 O = mfma16(Mf, Nh, rqR * Q);
+        const f32x4 O = mfma16(Mf, to_bf16x4(N), rqR * Q);
         // rows past the sequence end are dropped by the range check (the
         // halves are taken from packed words: storing bf16 vector elements
         // directly through the 16-bit buffer store is miscompiled)
@@ -546,22 +570,18 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
               ov[jj], odst,
               ((unsigned(t0) + unsigned(4 * g4 + jj)) * unsigned(rowstride) + colb + 16 * NSW * u) * 2u,
               0, 0);
-        // S <- Diag(e^{G_last}) S + K'^T N', two-term split on both sides:
-        // K'h N'h + K'l N'h as one 32-deep product (k-slots: this lane group's
-        // four tokens, high part then low part), then K'h N'l as a 32-deep
-        // product with a zero half.  (Both are 16x16x32: on gfx950 a 16x16x16
-        // product accumulating straight onto a 16x16x32 result was observed to
-        // return wrong sums.)
-        const bf16x8 Nhh = cat(Nh, Nh), Nl0 = cat(Nl, bf16x4{});
+        // S <- Diag(e^{G_last}) S + K'^T N in fp16 operands (kKpScale K' and
+        // kNScale N; k-slots: this lane group's four tokens).  The accumulator
+        // comes from the VALU (S gm), never straight from a product of another
+        // MFMA shape: on gfx950 a 16x16x16 product accumulating onto a
+        // 16x16x32 result was observed to return wrong sums.
+        const f16x4 Nq = f16x4{(_Float16)(N[0] * kNScale), (_Float16)(N[1] * kNScale),
+                               (_Float16)(N[2] * kNScale), (_Float16)(N[3] * kNScale)};
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
           const f32x4 gm = *reinterpret_cast<const f32x4*>(&P.gam[16 * rt + 4 * g4]);
-          const bf16x4 ah = *reinterpret_cast<const bf16x4*>(&P.kph[frag(rt, l16, 4 * g4)]);
-          const bf16x4 al = *reinterpret_cast<const bf16x4*>(&P.kpl[frag(rt, l16, 4 * g4)]);
-          f32x4 s = S[u][rt] * gm;
-          s = mfma32(cat(ah, al), Nhh, s);
-          s = mfma32(cat(ah, bf16x4{}), Nl0, s);
-          S[u][rt] = s;
+          const f16x4 a = *reinterpret_cast<const f16x4*>(&P.kp[frag(rt, l16, 4 * g4)]);
+          S[u][rt] = mfma16h(a, Nq, S[u][rt] * gm);
         }
       }
     }
@@ -569,13 +589,13 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
 
   load_round(va, 0);
   __syncthreads();
-  for (int r = 1; r <= nr; r += 2) {
+  for (int r = 1; r <= nr; r += 2) {  // r odd: buffer 0; r + 1: buffer 1
     load_round(vbuf, r);
-    consume_round(va, r);
+    consume_round(va, r, BufIdx<0>{});
     __syncthreads();
     if (r + 1 <= nr) {
       load_round(va, r + 1);
-      consume_round(vbuf, r + 1);
+      consume_round(vbuf, r + 1, BufIdx<1>{});
       __syncthreads();
     }
   }
