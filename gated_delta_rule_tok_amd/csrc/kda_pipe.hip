@@ -408,7 +408,9 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
     __syncthreads();
     if (tid < N && rank == target) seq_sh[0] = tid;
     __syncthreads();
-    n = seq_sh[0];
+    // uniform by construction; as a scalar, every address and buffer
+    // resource derived from it stays in scalar registers
+    n = __builtin_amdgcn_readfirstlane(seq_sh[0]);
   }
 
 
