@@ -114,8 +114,9 @@ kda_status_t kda_chunk_prefill_fwd(const void* q, const void* k, const void* v, 
   if (num_tokens > 0 && (!q || !k || !v || !g || !beta_logits || !out)) return KDA_ERR_INVALID_ARG;
   if (!A_log || !dt_bias || !cu_seqlens || !final_state) return KDA_ERR_INVALID_ARG;
   if (heads <= 0 || heads > 65536 || num_seqs <= 0) return KDA_ERR_INVALID_ARG;
-  // the kernels address token rows with 32-bit element offsets
-  if (num_tokens * int64_t(heads) * KDA_HEAD_DIM > INT32_MAX) return KDA_ERR_INVALID_ARG;
+  // the kernels address token rows with 32-bit byte offsets, also rows up to
+  // 256 past a sequence's end (range-checked reads that return zeros)
+  if ((num_tokens + 256) * int64_t(heads) * KDA_HEAD_DIM > INT32_MAX) return KDA_ERR_INVALID_ARG;
   // grid size: one workgroup per (sequence, head, value slice), up to 8 slices
   if (int64_t(num_seqs) * heads * 8 > INT32_MAX) return KDA_ERR_INVALID_ARG;
   if (state_dtype != KDA_STATE_FP32 && state_dtype != KDA_STATE_BF16) return KDA_ERR_INVALID_ARG;

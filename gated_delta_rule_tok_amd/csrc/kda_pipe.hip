@@ -14,17 +14,19 @@
 //   O = scale (e^G q) S + M N
 //   S <- Diag(e^{G_last}) S + (e^{G_last - G} k)^T N
 //
-// Work split.  One workgroup per (sequence, head, value slice).  Waves 0-3
-// ("producers") each take every fourth 16-token chunk and build the chunk's
-// package in LDS: the gate, the cumulative decay, the decayed operands, the
-// 16x16 products A and M, the inverse (I + A)^-1, and the norms.  None of it
-// depends on the state.  The remaining waves ("state waves", one or two
-// 16-column strips of the value slice each) walk the chunks in order, keeping
-// their strip of S (128 x 16 fp32) in registers, and apply the three state
-// contractions and the output.  Packages are double-buffered per round of
-// four chunks: in round r the producers write round r while the state waves
-// read round r-1; one workgroup barrier ends each round.  On gfx950 this puts
-// a VALU-heavy producer wave and an MFMA-heavy state wave on every SIMD.
+// Work split.  One workgroup per (sequence, head, value slice).  Eight
+// "producer" waves build the packages of a round of four 16-token chunks in
+// LDS, two per chunk (one per 64-channel half): first the norms, the gate,
+// the cumulative decay and the decayed operands of their channels, then,
+// after a workgroup barrier, one forms the 16x16 products A, A^T and the
+// inverse (I + A)^-1, the other M.  None of it depends on the state.  The
+// remaining waves ("state waves", one or two 16-column strips of the value
+// slice each) walk the chunks of the previous round in order, keeping their
+// strip of S (128 x 16 fp32) in registers, and apply the three state
+// contractions and the output: three chunks before the producers' mid-round
+// barrier, one after.  Packages are double-buffered per round; a second
+// barrier ends each round.  Each SIMD runs the two VALU-heavy producer waves
+// of one chunk and one MFMA-heavy state wave.
 //
 // Norms.  k is normalised before it enters any product (k~ = k / ||k||, the
 // norm from a dot-product pass over the row); q's norm is applied after the
@@ -56,7 +58,10 @@ namespace kda {
 namespace {
 
 constexpr int kTok = 16;  // tokens per chunk
-constexpr int kPW = 4;    // producer waves = chunks per round
+constexpr int kPW = 4;    // chunks per round
+constexpr int kPH = 2;    // producer waves per chunk (64-channel halves)
+constexpr int kProdWaves = kPW * kPH;
+constexpr int kEarly = 3;  // chunks the state waves apply before the producers' mid-round barrier
 constexpr float kKpScale = 16.f;     // K' enters the fp16 state update times this
 constexpr float kNScale = 0.0625f;   // ... and N times this (exact inverse)
 
@@ -65,7 +70,7 @@ struct Cfg {
   static constexpr int NS = VS / 16;             // 16-column strips in the slice
   static constexpr int NSW = NS < 4 ? NS : 4;    // state waves
   static constexpr int SPW = NS / NSW;           // strips per state wave
-  static constexpr int kThreads = 64 * (kPW + NSW);
+  static constexpr int kThreads = 64 * (kProdWaves + NSW);
 };
 
 // [128][16] tiles (row = key channel, column = token): rows are stored in the
@@ -98,42 +103,49 @@ struct BufIdx {
   static constexpr int value = B;
 };
 
-// One chunk's package: written by one producer wave, read by the state waves.
+// One chunk's package: written by the chunk's two producer waves, read by
+// the state waves.
 struct Pack {
   bf16 x[128 * kTok];    // X = e^{G} k~, swizzled rows
   bf16 qt[128 * kTok];   // Q_T = e^{G} q, swizzled rows
-  bf16 kp[128 * kTok];   // kKpScale K' as fp16, fragment order (block = 16 keys);
-                         // before that, scratch for K_G (bf16, swizzled rows)
+  bf16 kp[128 * kTok];   // kKpScale K' as fp16, fragment order (block = 16 keys)
   bf16 l[256];           // L, fragment order
   bf16 m[256];           // M', fragment order
   float beta[kTok];
-  float rk[kTok];        // 1 / ||k_t|| (producer scratch)
   float rqs[kTok];       // scale / ||q_t||
+  float rk[kPH][kTok];   // 1 / ||k_t||, one copy per producer wave (scratch)
   float gam[128];        // e^{G_last}
 };
 static_assert(sizeof(Pack::gam) >= sizeof(int) * (kInlineRankMax + 1), "rank scratch fits in gam");
 
-// Raw inputs of one chunk for one producer lane: tokens 8 th + rr of channels
-// 4 cg .. 4 cg + 3 (cg = lane / 2, th = lane % 2); q and k again as rows for
-// the norms (token lane / 4, channels 32 (lane % 4) ..); the beta logit of
-// token `lane` (lanes < 16).
+// Raw inputs of one chunk for one producer lane of channel half hf: tokens
+// 4 tq + rr (rr = 0..3) of channels 64 hf + 4 cg .. + 3 (cg = lane % 16,
+// tq = lane / 16, so each load instruction reads four 128-byte row segments,
+// 16 consecutive lanes each); k again as rows for its norm (token lane / 4,
+// channels 32 (lane % 4) ..); for the second half q as rows as well, for the
+// first the beta logit of token `lane` (lanes < 16).
 struct Raw {
-  uint2 q[8], k[8], g[8];
-  uint4 qn[4], kn[4];
+  uint2 q[4], k[4], g[4];
+  uint4 kn[4], qn[4];
   uint32_t beta;
 };
 
+// Head h's rows, bounded at the sequence end.  qn and beta: the q rows for
+// the second channel half, the beta logits for the first; the other half gets
+// an empty resource (its loads return zeros without touching memory), so the
+// loads need no branch (a branch here makes the compiler copy, and so wait
+// for, the loaded registers).
 struct RawSrc {
-  __amdgpu_buffer_rsrc_t q, k, g, beta;  // head h, bounded at the sequence end
+  __amdgpu_buffer_rsrc_t q, k, g, qn, beta;
 };
 
 // Rows past the sequence end read as zeros (buffer range check).
 __device__ __forceinline__ void load_raw(Raw& r, const RawSrc& src, int rowstride, int H, int t0,
-                                         int lane) {
-  const unsigned ch = 4u * unsigned(lane >> 1), th = unsigned(lane & 1);
+                                         int lane, int hf) {
+  const unsigned ch = 64u * unsigned(hf) + 4u * unsigned(lane & 15), tq = unsigned(lane >> 4);
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) {
-    const unsigned off = ((unsigned(t0) + 8u * th + rr) * unsigned(rowstride) + ch) * 2u;
+  for (int rr = 0; rr < 4; ++rr) {
+    const unsigned off = ((unsigned(t0) + 4u * tq + rr) * unsigned(rowstride) + ch) * 2u;
     r.q[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.q, off, 0, 0));
     r.k[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.k, off, 0, 0));
     r.g[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.g, off, 0, 0));
@@ -141,10 +153,11 @@ __device__ __forceinline__ void load_raw(Raw& r, const RawSrc& src, int rowstrid
   const unsigned offn =
       ((unsigned(t0) + unsigned(lane >> 2)) * unsigned(rowstride) + 32u * unsigned(lane & 3)) * 2u;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r.qn[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src.q, offn + 16u * i, 0, 0));
+  for (int i = 0; i < 4; ++i)
     r.kn[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src.k, offn + 16u * i, 0, 0));
-  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r.qn[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src.qn, offn + 16u * i, 0, 0));
   r.beta = __builtin_amdgcn_raw_buffer_load_b16(src.beta, (unsigned(t0) + unsigned(lane)) * unsigned(H) * 2u, 0, 0);
 }
 
@@ -161,11 +174,30 @@ __device__ __forceinline__ uint32_t pk2h(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, f16x2{(_Float16)lo, (_Float16)hi});
 }
 
-// Sum over the four lanes 4 i .. 4 i + 3.
+// Value of another lane of the same quad (DPP quad_perm pattern CTRL).
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the four lanes of a quad.
 __device__ __forceinline__ float quad_sum(float s) {
-  s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0xB1, 0xF, 0xF, false));
-  s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x4E, 0xF, 0xF, false));
+  s += quad_perm<0xB1>(s);  // [1,0,3,2]
+  s += quad_perm<0x4E>(s);  // [2,3,0,1]
   return s;
+}
+
+// sum over the row of 32 channels held by each lane of a quad
+__device__ __forceinline__ float row_norm2(const uint4* w) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s = dot2(w[i].x, s);
+    s = dot2(w[i].y, s);
+    s = dot2(w[i].z, s);
+    s = dot2(w[i].w, s);
+  }
+  return quad_sum(s);
 }
 
 // Channel i (0..3) of a 4-channel bf16 group.
@@ -174,54 +206,37 @@ __device__ __forceinline__ float chan(uint2 w, int i) {
   return (i & 1) ? bf16_hi(d) : bf16_lo(d);
 }
 
-// Values a producer keeps in registers across its MFMA step: kKpScale K' as
-// packed fp16 pairs of consecutive tokens, per channel.
-struct Held {
-  uint32_t kp[4][4];
-};
-
-// Producer, first half: norms of q and k, beta, the gate and its cumulative
-// sum, and every decayed operand.  Writes X = e^G k~ and Q_T = e^G q (which
-// are also the left operands of the A and M products), the scratch right
-// operand K_G = e^{-G} k~, gam, beta and rqs; returns K' in `held`.  FULL:
-// all 16 tokens are inside the sequence (no masking).
+// Producer, first phase (both waves of a chunk, one channel half each): the
+// norm of k (and of q, or beta), the gate and its cumulative sum, and every
+// decayed operand of the half's 64 channels.  Writes X = e^G k~ and Q_T =
+// e^G q, the products' right operand K_G = e^{-G} k~ (to `kg`), kKpScale K'
+// (fp16), gam, and rqs (second half) or beta (first half).  FULL: all 16
+// tokens are inside the sequence (no masking).
 template <bool FULL>
-__device__ __forceinline__ void produce_operands(Pack& pk, const Raw& raw, Held& held, int Lc,
-                                                 int lane, const float* c2, float c1, float lb2,
-                                                 float scale) {
-  const int cg = lane >> 1, th = lane & 1;
+__device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, float* tots, const Raw& raw,
+                                                 int hf, int Lc, int lane, const float* c2, float c1,
+                                                 float lb2, float scale) {
+  const int cg = lane & 15, tq = lane >> 4;
 
-  // scale / ||q_t|| and 1 / ||k_t|| for token lane/4: four lanes hold 32
-  // channels each
+  // 1 / ||k_t|| and scale / ||q_t|| or beta_t for token lane/4 (beta: lane)
   {
-    float sq = 0.f, sk = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sq = dot2(raw.qn[i].x, sq);
-      sq = dot2(raw.qn[i].y, sq);
-      sq = dot2(raw.qn[i].z, sq);
-      sq = dot2(raw.qn[i].w, sq);
-      sk = dot2(raw.kn[i].x, sk);
-      sk = dot2(raw.kn[i].y, sk);
-      sk = dot2(raw.kn[i].z, sk);
-      sk = dot2(raw.kn[i].w, sk);
-    }
-    sq = quad_sum(sq);
-    sk = quad_sum(sk);
-    if ((lane & 3) == 0) {
-      pk.rqs[lane >> 2] = rsqrtf(sq + kNormEps) * scale;
-      pk.rk[lane >> 2] = rsqrtf(sk + kNormEps);
-    }
-    if (lane < kTok)
+    const float sk = row_norm2(raw.kn);
+    if ((lane & 3) == 0) pk.rk[hf][lane >> 2] = rsqrtf(sk + kNormEps);
+    if (hf) {
+      const float sq = row_norm2(raw.qn);
+      if ((lane & 3) == 0) pk.rqs[lane >> 2] = rsqrtf(sq + kNormEps) * scale;
+    } else if (lane < kTok) {
       pk.beta[lane] = lane < Lc ? rcp(1.f + ex2(-kLog2e * bf16_to_f32(uint16_t(raw.beta)))) : 0.f;
+    }
   }
 
-  // gate sigma per (token, channel) and its running sum over this lane's 8
-  // tokens; the log2 decay of a token is lb2 * sigma (lb2 = lower_bound log2 e)
-  float cs[4][8];
+  // gate sigma per (token, channel), its running sum over this lane's 4
+  // tokens, then the sum over the earlier token groups (lanes 16 apart, via
+  // LDS); the log2 decay of a token is lb2 * sigma (lb2 = lower_bound log2 e)
+  float cs[4][4];
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) {
-    const bool valid = FULL || 8 * th + rr < Lc;
+  for (int rr = 0; rr < 4; ++rr) {
+    const bool valid = FULL || 4 * tq + rr < Lc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float sg = rcp(1.f + ex2(fmaf(chan(raw.g[rr], i), c1, c2[i])));
@@ -229,146 +244,157 @@ __device__ __forceinline__ void produce_operands(Pack& pk, const Raw& raw, Held&
       cs[i][rr] = rr == 0 ? inc : cs[i][rr - 1] + inc;
     }
   }
-
-  // G relative to the chunk start.  Lane th = 0 holds tokens 0..7, lane
-  // th = 1 tokens 8..15 and adds the partner's total of tokens 0..7.
+  // tots[g][4 cg + i]: the 4-token total of group g for channel 4 cg + i
+  *reinterpret_cast<f32x4*>(&tots[64 * tq + 4 * cg]) = f32x4{cs[0][3], cs[1][3], cs[2][3], cs[3][3]};
+  __builtin_amdgcn_wave_barrier();
+  f32x4 excl = {0.f, 0.f, 0.f, 0.f}, all = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(&tots[64 * g + 4 * cg]);
+    all += t;
+    if (g < tq) excl += t;
+  }
   float off[4], gam[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float own = cs[i][7], other = pair_swap(own);
-    off[i] = th ? lb2 * other : 0.f;
-    gam[i] = ex2(lb2 * (own + other));  // e^{G_last}
+    off[i] = lb2 * excl[i];
+    gam[i] = ex2(lb2 * all[i]);  // e^{G_last}
   }
-  if (th == 0) *reinterpret_cast<f32x4*>(&pk.gam[4 * cg]) = f32x4{gam[0], gam[1], gam[2], gam[3]};
+  if (tq == 0)
+    *reinterpret_cast<f32x4*>(&pk.gam[64 * hf + 4 * cg]) = f32x4{gam[0], gam[1], gam[2], gam[3]};
 
-  // 1 / ||k|| of this lane's 8 tokens (written above by other lanes of this wave)
+  // 1 / ||k|| of this lane's 4 tokens (written above by other lanes of this wave)
   __builtin_amdgcn_wave_barrier();
-  const f32x4 rk0 = *reinterpret_cast<const f32x4*>(&pk.rk[8 * th]);
-  const f32x4 rk1 = *reinterpret_cast<const f32x4*>(&pk.rk[8 * th + 4]);
+  const f32x4 rk4 = *reinterpret_cast<const f32x4*>(&pk.rk[hf][4 * tq]);
 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = swz(4 * cg + i) * kTok + 8 * th;  // this lane's 8 tokens of channel 4cg+i
+    const int c = 64 * hf + 4 * cg + i;
+    const int row = swz(c) * kTok + 4 * tq;  // this lane's 4 tokens of channel c
     const float g16 = kKpScale * gam[i];
-    uint32_t xk[4], qk[4], kg[4];
+    float vx[4], vq[4], vg[4], vk[4];
 #pragma unroll
-    for (int pr = 0; pr < 4; ++pr) {
-      float vx[2], vq[2], vg[2], vkp[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int rr = 2 * pr + h;
-        const float G = fmaf(cs[i][rr], lb2, off[i]);
-        const float E = ex2(G), F = ex2(-G);
-        const float kv = chan(raw.k[rr], i) * (rr < 4 ? rk0[rr] : rk1[rr - 4]);
-        const float qv = chan(raw.q[rr], i);
-        vx[h] = kv * E;
-        vq[h] = qv * E;
-        vg[h] = kv * F;
-        vkp[h] = vg[h] * g16;
-      }
-      xk[pr] = pk2(vx[0], vx[1]);
-      qk[pr] = pk2(vq[0], vq[1]);
-      kg[pr] = pk2(vg[0], vg[1]);
-      held.kp[i][pr] = pk2h(vkp[0], vkp[1]);
+    for (int rr = 0; rr < 4; ++rr) {
+      const float G = fmaf(cs[i][rr], lb2, off[i]);
+      const float E = ex2(G), F = ex2(-G);
+      const float kv = chan(raw.k[rr], i) * rk4[rr];
+      const float qv = chan(raw.q[rr], i);
+      vx[rr] = kv * E;
+      vq[rr] = qv * E;
+      vg[rr] = kv * F;
+      vk[rr] = vg[rr] * g16;
     }
-    *reinterpret_cast<uint4*>(&pk.x[row]) = uint4{xk[0], xk[1], xk[2], xk[3]};
-    *reinterpret_cast<uint4*>(&pk.qt[row]) = uint4{qk[0], qk[1], qk[2], qk[3]};
-    *reinterpret_cast<uint4*>(&pk.kp[row]) = uint4{kg[0], kg[1], kg[2], kg[3]};
+    *reinterpret_cast<uint2*>(&pk.x[row]) = uint2{pk2(vx[0], vx[1]), pk2(vx[2], vx[3])};
+    *reinterpret_cast<uint2*>(&pk.qt[row]) = uint2{pk2(vq[0], vq[1]), pk2(vq[2], vq[3])};
+    *reinterpret_cast<uint2*>(&kg[row]) = uint2{pk2(vg[0], vg[1]), pk2(vg[2], vg[3])};
+    *reinterpret_cast<uint2*>(&pk.kp[frag(c >> 4, c & 15, 4 * tq)]) =
+        uint2{pk2h(vk[0], vk[1]), pk2h(vk[2], vk[3])};
   }
 }
 
-// Producer, second half: the A and M products, the inverse and L, then K'
-// over the scratch operand (this wave's own LDS accesses are
-// processed in order, so the scratch reads are done before it is
-// overwritten).
-__device__ __forceinline__ void produce_products(Pack& pk, const Held& held, int lane) {
+// Producer, second phase, first wave of a chunk: A = X K_G^T and A^T over the
+// 128 channels, the inverse (I + A)^-1 and L.
+__device__ __forceinline__ void produce_inverse(Pack& pk, const bf16* kg, int lane) {
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int cg = lane >> 1, th = lane & 1;
 
-  // A = X K_G^T, A^T = K_G X^T and M'^T = K_G Q_T^T over the 128 channels;
   // k-slots 8 g4 .. 8 g4 + 7 of each 32-channel block, on both sides
-  __builtin_amdgcn_wave_barrier();  // the operands were written by other lanes of this wave
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  f32x4 accA = zero, accAt = zero, accMt = zero;
+  f32x4 accA = zero, accAt = zero;
   const int col = 4 * (l16 & 3);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const int r1 = 32 * kb + 8 * g4 + (l16 >> 2), r2 = r1 + 4;
     const int o1 = swz(r1) * kTok + col, o2 = swz(r2) * kTok + col;
     const bf16x8 KE = cat(tr4(&pk.x[o1]), tr4(&pk.x[o2]));
-    const bf16x8 KG = cat(tr4(&pk.kp[o1]), tr4(&pk.kp[o2]));
-    const bf16x8 QE = cat(tr4(&pk.qt[o1]), tr4(&pk.qt[o2]));
+    const bf16x8 KG = cat(tr4(&kg[o1]), tr4(&kg[o2]));
     accA = mfma32(KE, KG, accA);     // [t = 4g4+j][i = l16]
     accAt = mfma32(KG, KE, accAt);   // [i = 4g4+j][t = l16]
-    accMt = mfma32(KG, QE, accMt);   // [i = 4g4+j][t = l16]
   }
 
-  // beta and rqs were written by other lanes of this wave (before the
-  // operand writes that the barrier above orders)
   const f32x4 bR = *reinterpret_cast<const f32x4*>(&pk.beta[4 * g4]);
-  const float bC = pk.beta[l16], rqC = pk.rqs[l16];
-
-  f32x4 Nn, Nt, Mv, I4;
+  const float bC = pk.beta[l16];
+  f32x4 Nn, Nt, I4;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 4 * g4 + j;
     Nn[j] = l16 < r ? bR[j] * accA[j] : 0.f;    // A[r][l16]
     Nt[j] = r < l16 ? bC * accAt[j] : 0.f;      // A[l16][r]
-    Mv[j] = r <= l16 ? rqC * accMt[j] : 0.f;                   // M'[l16][r]
     I4[j] = r == l16 ? 1.f : 0.f;
   }
-  *reinterpret_cast<bf16x4*>(&pk.m[frag(0, l16, 4 * g4)]) = to_bf16x4(Mv);
 
   // (I + A)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8) (A^16 = 0).  Each product is
   // formed together with its transpose: an accumulator holds Z[4g+j][l16],
   // which is Z's B-operand layout and Z^T's A-operand layout, so Z = X Y is
   // mfma(X^T, Y) and Z^T = Y^T X^T is mfma(Y, X^T).
-  {
-    const bf16x4 nb = to_bf16x4(Nn), ntb = to_bf16x4(Nt);
-    const f32x4 N2 = mfma16(ntb, nb, zero), N2t = mfma16(nb, ntb, zero);
-    const bf16x4 n2b = to_bf16x4(N2), n2tb = to_bf16x4(N2t);
-    const f32x4 N4 = mfma16(n2tb, n2b, zero), N4t = mfma16(n2b, n2tb, zero);
-    const bf16x4 n4b = to_bf16x4(N4), n4tb = to_bf16x4(N4t);
-    const f32x4 N8 = mfma16(n4tb, n4b, zero);
-    const f32x4 P1t = mfma16(n2b, to_bf16x4(-Nt), I4 - Nt + N2t);   // (I - A)(I + A^2)
-    const bf16x4 p1tb = to_bf16x4(P1t);
-    const f32x4 P2t = mfma16(n4b, p1tb, P1t);                        // ... (I + A^4)
-    const bf16x4 p2tb = to_bf16x4(P2t), n8b = to_bf16x4(N8);
-    const f32x4 Dt = mfma16(n8b, p2tb, P2t);                         // D^T: D[l16][4g4+j]
-    // L[t][i] = (D - I)[t][i] b_i at fragment (m = t = l16, k = i = 4g4 + j)
-    *reinterpret_cast<bf16x4*>(&pk.l[frag(0, l16, 4 * g4)]) = to_bf16x4((Dt - I4) * bR);
-  }
-
-  // K' over K_G (this wave's scratch reads above come first in its LDS order)
-  __builtin_amdgcn_wave_barrier();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = 4 * cg + i;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int o = frag(c >> 4, c & 15, 8 * th + 4 * hh);
-      *reinterpret_cast<uint2*>(&pk.kp[o]) = uint2{held.kp[i][2 * hh], held.kp[i][2 * hh + 1]};
-    }
-  }
+  const bf16x4 nb = to_bf16x4(Nn), ntb = to_bf16x4(Nt);
+  const f32x4 N2 = mfma16(ntb, nb, zero), N2t = mfma16(nb, ntb, zero);
+  const bf16x4 n2b = to_bf16x4(N2), n2tb = to_bf16x4(N2t);
+  const f32x4 N4 = mfma16(n2tb, n2b, zero), N4t = mfma16(n2b, n2tb, zero);
+  const bf16x4 n4b = to_bf16x4(N4), n4tb = to_bf16x4(N4t);
+  const f32x4 N8 = mfma16(n4tb, n4b, zero);
+  const f32x4 P1t = mfma16(n2b, to_bf16x4(-Nt), I4 - Nt + N2t);   // (I - A)(I + A^2)
+  const bf16x4 p1tb = to_bf16x4(P1t);
+  const f32x4 P2t = mfma16(n4b, p1tb, P1t);                        // ... (I + A^4)
+  const bf16x4 p2tb = to_bf16x4(P2t), n8b = to_bf16x4(N8);
+  const f32x4 Dt = mfma16(n8b, p2tb, P2t);                         // D^T: D[l16][4g4+j]
+  // L[t][i] = (D - I)[t][i] b_i at fragment (m = t = l16, k = i = 4g4 + j)
+  *reinterpret_cast<bf16x4*>(&pk.l[frag(0, l16, 4 * g4)]) = to_bf16x4((Dt - I4) * bR);
 }
 
-// Value strip of one chunk for a state lane: tokens 4 g4 + j of one column,
-// one register each, raw bf16 bits (zero past the sequence end).  Nothing
-// combines the values here, so nothing waits for these loads before the
-// chunk that uses them.
-__device__ __forceinline__ void load_v4(uint32_t* e, __amdgpu_buffer_rsrc_t v, unsigned col,
-                                        int rowstride, int t0, int g4) {
+// Producer, second phase, second wave of a chunk: M' = rqs (Q_T K_G^T).
+__device__ __forceinline__ void produce_m(Pack& pk, const bf16* kg, int lane) {
+  const int l16 = lane & 15, g4 = lane >> 4;
+  f32x4 accMt = {0.f, 0.f, 0.f, 0.f};
+  const int col = 4 * (l16 & 3);
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    e[j] = __builtin_amdgcn_raw_buffer_load_b16(
-        v, ((unsigned(t0) + unsigned(4 * g4 + j)) * unsigned(rowstride) + col) * 2u, 0, 0);
+  for (int kb = 0; kb < 4; ++kb) {
+    const int r1 = 32 * kb + 8 * g4 + (l16 >> 2), r2 = r1 + 4;
+    const int o1 = swz(r1) * kTok + col, o2 = swz(r2) * kTok + col;
+    const bf16x8 KG = cat(tr4(&kg[o1]), tr4(&kg[o2]));
+    const bf16x8 QE = cat(tr4(&pk.qt[o1]), tr4(&pk.qt[o2]));
+    accMt = mfma32(KG, QE, accMt);   // [i = 4g4+j][t = l16]
+  }
+  const float rqC = pk.rqs[l16];
+  f32x4 Mv;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) Mv[j] = 4 * g4 + j <= l16 ? rqC * accMt[j] : 0.f;   // M'[l16][4g4+j]
+  *reinterpret_cast<bf16x4*>(&pk.m[frag(0, l16, 4 * g4)]) = to_bf16x4(Mv);
 }
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Value strip (16 tokens x 16 columns) of one chunk as rows: lane L holds
+// columns 4 (L % 4) .. + 3 of token L / 4, one 8-byte load (zero past the
+// sequence end).
+__device__ __forceinline__ uint2 load_vrow(__amdgpu_buffer_rsrc_t v, unsigned c0, int rowstride,
+                                           int t0, int lane) {
+  const unsigned off =
+      ((unsigned(t0) + unsigned(lane >> 2)) * unsigned(rowstride) + c0 + 4u * unsigned(lane & 3)) * 2u;
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(v, off, 0, 0));
+}
+
+// Per state wave and strip: 16 x 16 bf16 tiles that turn the row-wise value
+// loads into the accumulator layout and the output back into rows, so global
+// memory sees 8-byte accesses only.
+struct Tiles {
+  bf16 v[256];  // V rows, row-major [token][column]
+  bf16 o[256];  // O, column-major [column][token]
+};
+
+template <int NSW, int SPW>
+struct Smem {
+  Pack pk[2][kPW];          // first: keeps the packages' alignment
+  bf16 kg[kPW][128 * kTok];  // K_G of the round being produced, swizzled rows
+  float tots[kPW][kPH][256]; // per producer wave: 4-token gate totals [group][channel]
+  Tiles t[NSW][SPW];
+};
 
 template <int VS>
 __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   using C = Cfg<VS>;
   constexpr int SPW = C::SPW, NSW = C::NSW;
-  __shared__ __attribute__((aligned(16))) Pack pk[2][kPW];
+  __shared__ __attribute__((aligned(16))) Smem<NSW, SPW> sm;
+  Pack (&pk)[2][kPW] = sm.pk;
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave index as a uniform (scalar) value: the two roles below run separate
@@ -420,34 +446,45 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   const int nr = (nc + kPW - 1) / kPW;            // rounds
   const int rowstride = H * kD;
 
-  if (wave < kPW) {
+  if (wave < kProdWaves) {
     // ---------------- producer waves ----------------
+    // wave = chunk slot c of the round + kPW * channel half hf; the two
+    // waves of a chunk share a SIMD
+    const int c = wave & (kPW - 1), hf = wave / kPW;
     RawSrc src;
     src.q = rows_rsrc(p.q + size_t(h) * kD, eos, rowstride, kD);
     src.k = rows_rsrc(p.k + size_t(h) * kD, eos, rowstride, kD);
     src.g = rows_rsrc(p.g + size_t(h) * kD, eos, rowstride, kD);
-    src.beta = rows_rsrc(p.beta + h, eos, H, 1);
+    src.qn = rows_rsrc(p.q + size_t(h) * kD, hf ? eos : 0, rowstride, kD);
+    src.beta = rows_rsrc(p.beta + h, hf ? 0 : eos, H, 1);
     const float eA = expf(p.A_log[h]);
     const float c1 = -kLog2e * eA;
     const float lb2 = p.lower_bound * kLog2e;
     float c2[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c2[i] = c1 * p.dt_bias[h * kD + 4 * (lane >> 1) + i];
+    for (int i = 0; i < 4; ++i) c2[i] = c1 * p.dt_bias[h * kD + 64 * hf + 4 * (lane & 15) + i];
     __builtin_amdgcn_sched_barrier(0);  // constants first: nothing waits behind the first chunk's loads
     Raw raw;
-    if (wave < nc) load_raw(raw, src, rowstride, H, bos + kTok * wave, lane);
+    if (c < nc) load_raw(raw, src, rowstride, H, bos + kTok * c, lane, hf);
+    bf16* kg = sm.kg[c];
+    float* tots = sm.tots[c][hf];
+    // two barriers per round: operands of both halves, then the products
     for (int r = 0; r <= nr; ++r) {
-      const int j = kPW * r + wave;
-      if (r < nr && j < nc) {
+      const int j = kPW * r + c;
+      const bool act = r < nr && j < nc;
+      Pack& P = pk[r & 1][c];
+      if (act) {
         const int t0 = bos + kTok * j, Lc = min(kTok, eos - t0);
-        Pack& P = pk[r & 1][wave];
-        Held held;
-        if (Lc == kTok) produce_operands<true>(P, raw, held, Lc, lane, c2, c1, lb2, p.scale);
-        else produce_operands<false>(P, raw, held, Lc, lane, c2, c1, lb2, p.scale);
+        if (Lc == kTok) produce_operands<true>(P, kg, tots, raw, hf, Lc, lane, c2, c1, lb2, p.scale);
+        else produce_operands<false>(P, kg, tots, raw, hf, Lc, lane, c2, c1, lb2, p.scale);
         // this wave's next chunk, one round ahead
         const int tn = t0 + kTok * kPW;
-        if (tn < eos) load_raw(raw, src, rowstride, H, tn, lane);
-        produce_products(P, held, lane);
+        if (tn < eos) load_raw(raw, src, rowstride, H, tn, lane, hf);
+      }
+      __syncthreads();
+      if (act) {
+        if (hf == 0) produce_inverse(P, kg, lane);
+        else produce_m(P, kg, lane);
       }
       __syncthreads();
     }
@@ -459,7 +496,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   // producer wave that shares their SIMD.
   __builtin_amdgcn_s_setprio(2);
   // S[u][rt][j] = S[16 rt + 4 g4 + j][column of strip u]
-  const int sw = wave - kPW;
+  const int sw = wave - kProdWaves;
   const int colb = slice * VS + 16 * sw + l16;  // column of strip 0; strip u adds 16 NSW u
   const __amdgpu_buffer_rsrc_t vsrc = rows_rsrc(p.v + size_t(h) * kD, eos, rowstride, kD);
   const __amdgpu_buffer_rsrc_t odst = rows_rsrc(p.out + size_t(h) * kD, eos, rowstride, kD);
@@ -497,30 +534,34 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   // values of each round's chunks, loaded one round before use into two
   // alternating register sets (no copies, so nothing waits for the output
   // stores issued in between)
-  uint32_t va[kPW][SPW][4], vbuf[kPW][SPW][4];
+  const unsigned cstrip = unsigned(slice * VS + 16 * sw);  // first column of strip 0
+  uint2 va[kPW][SPW], vbuf[kPW][SPW];
 #pragma unroll
   for (int c = 0; c < kPW; ++c)
 #pragma unroll
-    for (int u = 0; u < SPW; ++u)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) va[c][u][j] = vbuf[c][u][j] = 0u;
+    for (int u = 0; u < SPW; ++u) va[c][u] = vbuf[c][u] = uint2{0u, 0u};
 
-  auto load_round = [&](uint32_t (&v)[kPW][SPW][4], int r) {
-    if (r >= nr) return;
+  // Unconditional: chunks past the sequence end read as zeros (range check);
+  // conditional loads would make the compiler wait for every outstanding
+  // memory operation (output stores included) before each load.
+  auto load_round = [&](uint2 (&v)[kPW][SPW], int r) {
 #pragma unroll
     for (int c = 0; c < kPW; ++c) {
       const int t0 = bos + kTok * (kPW * r + c);
-      if (t0 < eos)
 #pragma unroll
-        for (int u = 0; u < SPW; ++u) load_v4(v[c][u], vsrc, colb + 16 * NSW * u, rowstride, t0, g4);
+      for (int u = 0; u < SPW; ++u) v[c][u] = load_vrow(vsrc, cstrip + 16 * NSW * u, rowstride, t0, lane);
     }
   };
-  // the chunks of round r - 1, in order, from package buffer B = (r - 1) % 2
-  // (a compile-time index, so every LDS read is a lane offset plus a constant)
-  auto consume_round = [&](const uint32_t (&v)[kPW][SPW][4], int r, auto buf) {
+  // chunks of round r - 1, in order, from package buffer B = (r - 1) % 2:
+  // the first kEarly while the producers form their operands, the rest while
+  // they form the products (compile-time indices, so every LDS read is a
+  // lane offset plus a constant)
+  auto consume_half = [&](const uint2 (&v)[kPW][SPW], int r, auto buf, auto half) {
     constexpr int B = decltype(buf)::value;
+    constexpr int HB = decltype(half)::value;
+    constexpr int C0 = HB ? kEarly : 0, C1 = HB ? kPW : kEarly;
 #pragma unroll
-    for (int c = 0; c < kPW; ++c) {
+    for (int c = C0; c < C1; ++c) {
       const int j = kPW * (r - 1) + c;
       if (j >= nc) break;
       const Pack& P = pk[B][c];
@@ -554,24 +595,26 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
           Y = mfma32(ax[kb2], Sb[kb2], Y);
           Q = mfma32(aq[kb2], Sb[kb2], Q);
         }
-        f32x4 V;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) V[jj] = bf16_lo(v[c][u][jj]);
+        // V in the accumulator layout: the row tile read back transposed
+        // (lane l16 of group g4: column l16 of tokens 4 g4 .. 4 g4 + 3); this
+        // wave's own LDS accesses are processed in order
+        Tiles& tl = sm.t[sw][u];
+        *reinterpret_cast<uint2*>(&tl.v[4 * lane]) = v[c][u];
+        __builtin_amdgcn_wave_barrier();
+        const f32x4 V = to_f32x4(tr4(&tl.v[4 * lane]));
         const f32x4 D = V - Y;
         const f32x4 N = mfma16(Lf, to_bf16x4(D), bR * D);
         const f32x4 O = mfma16(Mf, to_bf16x4(N), rqR * Q);
-        // rows past the sequence end are dropped by the range check (the
-        // halves are taken from packed words: storing bf16 vector elements
-        // directly through the 16-bit buffer store is miscompiled)
-        const uint32_t w01 = pk2(O[0], O[1]), w23 = pk2(O[2], O[3]);
-        const unsigned short ov[4] = {(unsigned short)w01, (unsigned short)(w01 >> 16),
-                                      (unsigned short)w23, (unsigned short)(w23 >> 16)};
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          __builtin_amdgcn_raw_buffer_store_b16(
-              ov[jj], odst,
-              ((unsigned(t0) + unsigned(4 * g4 + jj)) * unsigned(rowstride) + colb + 16 * NSW * u) * 2u,
-              0, 0);
+        // O into rows: written column-major, read back transposed (lane l16
+        // of group g4: columns 4 g4 .. + 3 of token l16), one 8-byte store
+        // per lane; rows past the sequence end are dropped by the range check
+        *reinterpret_cast<uint2*>(&tl.o[16 * l16 + 4 * g4]) = uint2{pk2(O[0], O[1]), pk2(O[2], O[3])};
+        __builtin_amdgcn_wave_barrier();
+        const bf16x4 orow = tr4(&tl.o[64 * g4 + 16 * (l16 >> 2) + 4 * (l16 & 3)]);
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(u32x2, orow), odst,
+            ((unsigned(t0) + unsigned(l16)) * unsigned(rowstride) + cstrip + 16 * NSW * u + 4u * g4) * 2u,
+            0, 0);
         // S <- Diag(e^{G_last}) S + K'^T N in fp16 operands (kKpScale K' and
         // kNScale N; k-slots: this lane group's four tokens).  The accumulator
         // comes from the VALU (S gm), never straight from a product of another
@@ -589,15 +632,22 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
     }
   };
 
+  // the producers' two barriers per round: half of the previous round's
+  // chunks before each
   load_round(va, 0);
+  __syncthreads();
   __syncthreads();
   for (int r = 1; r <= nr; r += 2) {  // r odd: buffer 0; r + 1: buffer 1
     load_round(vbuf, r);
-    consume_round(va, r, BufIdx<0>{});
+    consume_half(va, r, BufIdx<0>{}, BufIdx<0>{});
+    __syncthreads();
+    consume_half(va, r, BufIdx<0>{}, BufIdx<1>{});
     __syncthreads();
     if (r + 1 <= nr) {
       load_round(va, r + 1);
-      consume_round(vbuf, r + 1, BufIdx<1>{});
+      consume_half(vbuf, r + 1, BufIdx<1>{}, BufIdx<0>{});
+      __syncthreads();
+      consume_half(vbuf, r + 1, BufIdx<1>{}, BufIdx<1>{});
       __syncthreads();
     }
   }

@@ -87,8 +87,9 @@ size_t kda_get_workspace_size(int64_t max_tokens, int32_t heads, int32_t max_seq
  *
  * q, k, v, g, beta_logits and out may be NULL when num_tokens is 0; every other
  * pointer except initial_state and workspace is required.  Size limits:
- * num_tokens * heads * 128 < 2^31 (token rows are addressed with 32-bit
- * element offsets), heads <= 65536, num_seqs * heads * 8 < 2^31.
+ * (num_tokens + 256) * heads * 128 < 2^31 (token rows, and rows up to 256
+ * past a sequence's end that the kernels read as zeros, are addressed with
+ * 32-bit byte offsets), heads <= 65536, num_seqs * heads * 8 < 2^31.
  *
  * Work is queued on the stream and the call returns without waiting: no host
  * synchronisation, no allocation and no device-to-host copy, so the call can be

@@ -99,6 +99,8 @@ def test_null_required_pointer_rejected(name):
     dict(sdt=2), dict(sdt=-1), dict(lb=float("nan")), dict(lb=float("-inf")),
     dict(scale=float("inf")), dict(scale=float("nan")), dict(N=2 ** 28, H=16),
     dict(T=2 ** 20, H=16), dict(T=2 ** 24, H=1),
+    # rows up to 256 past the end must stay addressable: (T + 256) H 128 < 2^31
+    dict(T=2 ** 24 - 100, H=1),
 ])
 def test_bad_sizes_and_scalars_rejected(over):
     assert _call(**over) == INVALID
