@@ -139,27 +139,49 @@ struct RawSrc {
   __amdgpu_buffer_rsrc_t q, k, g, qn, beta;
 };
 
-// Rows past the sequence end read as zeros (buffer range check).
-__device__ __forceinline__ void load_raw(Raw& r, const RawSrc& src, int rowstride, int H, int t0,
-                                         int lane, int hf) {
-  const unsigned ch = 64u * unsigned(hf) + 4u * unsigned(lane & 15), tq = unsigned(lane >> 4);
+// Loads of one chunk's raw inputs, in three groups so that a chunk's loads
+// can be issued while the previous chunk's operands are formed, each group as
+// soon as its registers have been consumed.  Rows past the sequence end read
+// as zeros (buffer range check), so the loads need no condition.
+struct RawLoad {
+  RawSrc src;
+  int rowstride, H, lane, hf;
+
+  // rows for the norms, and beta
+  __device__ __forceinline__ void rows(Raw& r, int t0) const {
+    const unsigned offn =
+        ((unsigned(t0) + unsigned(lane >> 2)) * unsigned(rowstride) + 32u * unsigned(lane & 3)) * 2u;
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const unsigned off = ((unsigned(t0) + 4u * tq + rr) * unsigned(rowstride) + ch) * 2u;
-    r.q[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.q, off, 0, 0));
-    r.k[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.k, off, 0, 0));
-    r.g[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.g, off, 0, 0));
+    for (int i = 0; i < 4; ++i) {
+      r.kn[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src.k, offn + 16u * i, 0, 0));
+      r.qn[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src.qn, offn + 16u * i, 0, 0));
+    }
+    r.beta = __builtin_amdgcn_raw_buffer_load_b16(src.beta, (unsigned(t0) + unsigned(lane)) * unsigned(H) * 2u, 0, 0);
   }
-  const unsigned offn =
-      ((unsigned(t0) + unsigned(lane >> 2)) * unsigned(rowstride) + 32u * unsigned(lane & 3)) * 2u;
+  __device__ __forceinline__ unsigned col_off(int t0, int rr) const {
+    const unsigned ch = 64u * unsigned(hf) + 4u * unsigned(lane & 15), tq = unsigned(lane >> 4);
+    return ((unsigned(t0) + 4u * tq + rr) * unsigned(rowstride) + ch) * 2u;
+  }
+  // gate inputs
+  __device__ __forceinline__ void gate(Raw& r, int t0) const {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r.kn[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src.k, offn + 16u * i, 0, 0));
+    for (int rr = 0; rr < 4; ++rr)
+      r.g[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.g, col_off(t0, rr), 0, 0));
+  }
+  // q and k
+  __device__ __forceinline__ void qk(Raw& r, int t0) const {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r.qn[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src.qn, offn + 16u * i, 0, 0));
-  r.beta = __builtin_amdgcn_raw_buffer_load_b16(src.beta, (unsigned(t0) + unsigned(lane)) * unsigned(H) * 2u, 0, 0);
-}
+    for (int rr = 0; rr < 4; ++rr) {
+      r.q[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.q, col_off(t0, rr), 0, 0));
+      r.k[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.k, col_off(t0, rr), 0, 0));
+    }
+  }
+  __device__ __forceinline__ void all(Raw& r, int t0) const {
+    rows(r, t0);
+    gate(r, t0);
+    qk(r, t0);
+  }
+};
 
 __device__ __forceinline__ float dot2(uint32_t a, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
@@ -213,9 +235,9 @@ __device__ __forceinline__ float chan(uint2 w, int i) {
 // (fp16), gam, and rqs (second half) or beta (first half).  FULL: all 16
 // tokens are inside the sequence (no masking).
 template <bool FULL>
-__device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, float* tots, const Raw& raw,
-                                                 int hf, int Lc, int lane, const float* c2, float c1,
-                                                 float lb2, float scale) {
+__device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, float* tots, Raw& raw,
+                                                 const RawLoad& ld, int tn, int hf, int Lc, int lane,
+                                                 const float* c2, float c1, float lb2, float scale) {
   const int cg = lane & 15, tq = lane >> 4;
 
   // 1 / ||k_t|| and scale / ||q_t|| or beta_t for token lane/4 (beta: lane)
@@ -244,6 +266,9 @@ __device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, float* tots
       cs[i][rr] = rr == 0 ? inc : cs[i][rr - 1] + inc;
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+  ld.gate(raw, tn);  // the next chunk's (tn), into the registers just consumed
+  __builtin_amdgcn_sched_barrier(0);
   // tots[g][4 cg + i]: the 4-token total of group g for channel 4 cg + i
   *reinterpret_cast<f32x4*>(&tots[64 * tq + 4 * cg]) = f32x4{cs[0][3], cs[1][3], cs[2][3], cs[3][3]};
   __builtin_amdgcn_wave_barrier();
@@ -290,6 +315,9 @@ __device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, float* tots
     *reinterpret_cast<uint2*>(&pk.kp[frag(c >> 4, c & 15, 4 * tq)]) =
         uint2{pk2h(vk[0], vk[1]), pk2h(vk[2], vk[3])};
   }
+  __builtin_amdgcn_sched_barrier(0);
+  ld.qk(raw, tn);
+  ld.rows(raw, tn);
 }
 
 // Producer, second phase, first wave of a chunk: A = X K_G^T and A^T over the
@@ -464,8 +492,9 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) c2[i] = c1 * p.dt_bias[h * kD + 64 * hf + 4 * (lane & 15) + i];
     __builtin_amdgcn_sched_barrier(0);  // constants first: nothing waits behind the first chunk's loads
+    const RawLoad ld{src, rowstride, H, lane, hf};
     Raw raw;
-    if (c < nc) load_raw(raw, src, rowstride, H, bos + kTok * c, lane, hf);
+    ld.all(raw, bos + kTok * c);
     bf16* kg = sm.kg[c];
     float* tots = sm.tots[c][hf];
     // two barriers per round: operands of both halves, then the products
@@ -475,11 +504,11 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
       Pack& P = pk[r & 1][c];
       if (act) {
         const int t0 = bos + kTok * j, Lc = min(kTok, eos - t0);
-        if (Lc == kTok) produce_operands<true>(P, kg, tots, raw, hf, Lc, lane, c2, c1, lb2, p.scale);
-        else produce_operands<false>(P, kg, tots, raw, hf, Lc, lane, c2, c1, lb2, p.scale);
-        // this wave's next chunk, one round ahead
+        // this wave's next chunk (one round ahead) is loaded while the
+        // operands are formed
         const int tn = t0 + kTok * kPW;
-        if (tn < eos) load_raw(raw, src, rowstride, H, tn, lane, hf);
+        if (Lc == kTok) produce_operands<true>(P, kg, tots, raw, ld, tn, hf, Lc, lane, c2, c1, lb2, p.scale);
+        else produce_operands<false>(P, kg, tots, raw, ld, tn, hf, Lc, lane, c2, c1, lb2, p.scale);
       }
       __syncthreads();
       if (act) {
