@@ -8,6 +8,10 @@ is no CPU fallback: if libkda.so is missing, every call raises.
     ws = torch.empty(kda_get_workspace_size(T, H, N), dtype=torch.uint8, device="cuda")
     kda_chunk_prefill_fwd(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, scale,
                           initial_state, cu_seqlens, out, final_state, ws)
+
+q, k, v, g, out and beta_logits may be strided views (channels contiguous, for
+[T, H, 128] both strides multiples of 8 elements): they then go through
+kda_chunk_prefill_fwd_strided, with no copy.
 """
 from __future__ import annotations
 
@@ -26,6 +30,13 @@ KDA_STATE_FP32 = 0
 KDA_STATE_BF16 = 1
 
 _lib = None
+
+
+class _Strides(ctypes.Structure):
+    """kda_strides_t of include/kda.h (element strides)."""
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "q_token", "q_head", "k_token", "k_head", "v_token", "v_head", "g_token", "g_head",
+        "beta_token", "beta_head", "out_token", "out_head")]
 
 
 class KdaError(RuntimeError):
@@ -66,6 +77,10 @@ def load_library():
         lib.kda_chunk_prefill_fwd.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P, P, P, P,
                                               I64, I32, I32, ctypes.c_int, SZ]
         lib.kda_chunk_prefill_fwd.restype = ctypes.c_int
+        lib.kda_chunk_prefill_fwd_strided.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P, P, P,
+                                                      P, I64, I32, I32, ctypes.c_int, SZ,
+                                                      ctypes.POINTER(_Strides)]
+        lib.kda_chunk_prefill_fwd_strided.restype = ctypes.c_int
         lib.kda_status_string.argtypes = [ctypes.c_int]
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_last_hip_error.argtypes = []
@@ -91,7 +106,8 @@ def kda_last_hip_error() -> str:
 
 
 def kda_debug_set_kernel(k: int) -> int:
-    """Test hook: 0/1 chunked MFMA kernel (default), 2 token-serial kernel."""
+    """Test hook: 0 pipelined 16-token kernel (default), 1 64-token kernel, 2
+    token-serial kernel."""
     prev = load_library().kda_debug_set_kernel(int(k))
     if prev < 0:
         raise ValueError(f"invalid kernel selector {k}")
@@ -106,7 +122,9 @@ def kda_debug_set_vsplit(s: int) -> int:
     return prev
 
 
-def _check(t, name, dtype, shape=None):
+def _check(t, name, dtype, shape=None, strided=False):
+    """Device pointer of t after the dtype/shape checks.  strided: the leading
+    two strides may be anything non-negative (the last dim must be dense)."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -114,10 +132,14 @@ def _check(t, name, dtype, shape=None):
         raise ValueError(f"{name} must be on a GPU device, got {t.device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous (dense row-major)")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if strided:
+        if t.numel() and (any(st < 0 for st in t.stride())
+                          or (t.dim() == 3 and t.stride(2) != 1 and t.shape[2] > 1)):
+            raise ValueError(f"{name} must have non-negative strides and contiguous channels")
+    elif not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (dense row-major)")
     return t.data_ptr()
 
 
@@ -158,18 +180,22 @@ def kda_chunk_prefill_fwd(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound: 
     else:
         raise TypeError(f"state dtype must be float32 or bfloat16, got {final_state.dtype}")
     sshape = (N, H, HEAD_DIM, HEAD_DIM)
+    if beta_logits.dim() == 3 and beta_logits.shape[0] == 1:
+        beta_logits = beta_logits[0]
+    if beta_logits.dim() == 3 and beta_logits.shape[-1] == 1:
+        beta_logits = beta_logits[..., 0]
+    views = {"q": q, "k": k, "v": v, "g": g, "beta": beta_logits, "out": out}
     ptrs = [
-        _check(q, "q", bf, (T, H, D)), _check(k, "k", bf, (T, H, D)),
-        _check(v, "v", bf, (T, H, D)), _check(g, "g", bf, (T, H, D)),
-        _check(beta_logits.reshape(T, H) if beta_logits.numel() == T * H else beta_logits,
-               "beta_logits", bf, (T, H)),
+        _check(q, "q", bf, (T, H, D), strided=True), _check(k, "k", bf, (T, H, D), strided=True),
+        _check(v, "v", bf, (T, H, D), strided=True), _check(g, "g", bf, (T, H, D), strided=True),
+        _check(beta_logits, "beta_logits", bf, (T, H), strided=True),
         _check(A_log.reshape(-1), "A_log", torch.float32, (H,)),
         _check(dt_bias.reshape(H, -1), "dt_bias", torch.float32, (H, D)),
     ]
     s0 = None if initial_state is None else _check(initial_state, "initial_state",
                                                    final_state.dtype, sshape)
     cu = _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
-    o = _check(out, "out", bf, (T, H, D))
+    o = _check(out, "out", bf, (T, H, D), strided=True)
     fs = _check(final_state, "final_state", final_state.dtype, sshape)
     if workspace is None:
         ws, wsb = None, 0
@@ -180,8 +206,17 @@ def kda_chunk_prefill_fwd(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound: 
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif isinstance(stream, torch.cuda.Stream):
         stream = stream.cuda_stream
-    rc = lib.kda_chunk_prefill_fwd(*ptrs, float(lower_bound), float(scale), s0, cu, o, fs, ws,
-                                   ctypes.c_void_p(int(stream)), T, H, N, sdt, wsb)
+    args = (*ptrs, float(lower_bound), float(scale), s0, cu, o, fs, ws,
+            ctypes.c_void_p(int(stream)), T, H, N, sdt, wsb)
+    if all(t.is_contiguous() for t in views.values()):
+        rc = lib.kda_chunk_prefill_fwd(*args)
+    else:
+        st = _Strides()
+        for name in ("q", "k", "v", "g", "out"):
+            setattr(st, f"{name}_token", views[name].stride(0))
+            setattr(st, f"{name}_head", views[name].stride(1))
+        st.beta_token, st.beta_head = views["beta"].stride(0), views["beta"].stride(1)
+        rc = lib.kda_chunk_prefill_fwd_strided(*args, ctypes.byref(st))
     if rc != KDA_OK:
         detail = lib.kda_last_hip_error().decode() if rc == 4 else ""
         raise KdaError(rc, f"kda_chunk_prefill_fwd: {kda_status_string(rc)} {detail}".strip())

@@ -101,13 +101,25 @@ int kda_debug_set_vsplit(int s) {
   return g_vsplit_override.exchange(s);
 }
 
-kda_status_t kda_chunk_prefill_fwd(const void* q, const void* k, const void* v, const void* g,
-                                   const void* beta_logits, const float* A_log,
-                                   const float* dt_bias, float lower_bound, float scale,
-                                   const void* initial_state, const int32_t* cu_seqlens, void* out,
-                                   void* final_state, void* workspace, void* stream,
-                                   int64_t num_tokens, int32_t heads, int32_t num_seqs,
-                                   kda_state_dtype_t state_dtype, size_t workspace_bytes) {
+}  // extern "C"
+
+namespace {
+
+// Stride checks of one [T, H, 128] tensor: non-negative multiples of 8
+// elements, and every row up to 256 past the end addressable with 32-bit
+// byte offsets.
+bool rows_ok(int64_t ts, int64_t hs, int64_t T, int64_t H, int64_t rowlen, int64_t align) {
+  if (ts < 0 || hs < 0 || ts % align || hs % align) return false;
+  return (T + 256) * ts + (H - 1) * hs + rowlen <= INT32_MAX;
+}
+
+kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
+                     const void* beta_logits, const float* A_log, const float* dt_bias,
+                     float lower_bound, float scale, const void* initial_state,
+                     const int32_t* cu_seqlens, void* out, void* final_state, void* workspace,
+                     void* stream, int64_t num_tokens, int32_t heads, int32_t num_seqs,
+                     kda_state_dtype_t state_dtype, size_t workspace_bytes,
+                     const kda_strides_t& sd) {
   // ---- checks (no HIP call before they pass) --------------------------------
   if (num_tokens < 0 || num_tokens > INT32_MAX) return KDA_ERR_INVALID_ARG;  // int32 offsets
   // per-token tensors may be empty (and NULL) only when there are no tokens
@@ -115,8 +127,19 @@ kda_status_t kda_chunk_prefill_fwd(const void* q, const void* k, const void* v, 
   if (!A_log || !dt_bias || !cu_seqlens || !final_state) return KDA_ERR_INVALID_ARG;
   if (heads <= 0 || heads > 65536 || num_seqs <= 0) return KDA_ERR_INVALID_ARG;
   // the kernels address token rows with 32-bit byte offsets, also rows up to
-  // 256 past a sequence's end (range-checked reads that return zeros)
-  if ((num_tokens + 256) * int64_t(heads) * KDA_HEAD_DIM > INT32_MAX) return KDA_ERR_INVALID_ARG;
+  // 256 past a sequence's end (range-checked reads that return zeros), with
+  // 8- and 16-byte accesses
+  const int64_t T = num_tokens, H = heads;
+  if (!rows_ok(sd.q_token, sd.q_head, T, H, KDA_HEAD_DIM, 8) ||
+      !rows_ok(sd.k_token, sd.k_head, T, H, KDA_HEAD_DIM, 8) ||
+      !rows_ok(sd.v_token, sd.v_head, T, H, KDA_HEAD_DIM, 8) ||
+      !rows_ok(sd.g_token, sd.g_head, T, H, KDA_HEAD_DIM, 8) ||
+      !rows_ok(sd.out_token, sd.out_head, T, H, KDA_HEAD_DIM, 8) ||
+      !rows_ok(sd.beta_token, sd.beta_head, T, H, 1, 1))
+    return KDA_ERR_INVALID_ARG;
+  for (const void* ptr : {q, k, v, g, static_cast<const void*>(out)})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16) return KDA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(beta_logits) % 2) return KDA_ERR_INVALID_ARG;
   // grid size: one workgroup per (sequence, head, value slice), up to 8 slices
   if (int64_t(num_seqs) * heads * 8 > INT32_MAX) return KDA_ERR_INVALID_ARG;
   if (state_dtype != KDA_STATE_FP32 && state_dtype != KDA_STATE_BF16) return KDA_ERR_INVALID_ARG;
@@ -147,6 +170,12 @@ kda_status_t kda_chunk_prefill_fwd(const void* q, const void* k, const void* v, 
   p.order = static_cast<int32_t*>(workspace);
   p.lower_bound = lower_bound;
   p.scale = scale;
+  p.ts_q = int(sd.q_token), p.hs_q = int(sd.q_head);
+  p.ts_k = int(sd.k_token), p.hs_k = int(sd.k_head);
+  p.ts_v = int(sd.v_token), p.hs_v = int(sd.v_head);
+  p.ts_g = int(sd.g_token), p.hs_g = int(sd.g_head);
+  p.ts_b = int(sd.beta_token), p.hs_b = int(sd.beta_head);
+  p.ts_o = int(sd.out_token), p.hs_o = int(sd.out_head);
   p.T = int(num_tokens);
   p.H = heads;
   p.N = num_seqs;
@@ -178,6 +207,37 @@ kda_status_t kda_chunk_prefill_fwd(const void* q, const void* k, const void* v, 
       return hip_failure(e, "pipelined chunk kernel launch");
   }
   return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_prefill_fwd(const void* q, const void* k, const void* v, const void* g,
+                                   const void* beta_logits, const float* A_log,
+                                   const float* dt_bias, float lower_bound, float scale,
+                                   const void* initial_state, const int32_t* cu_seqlens, void* out,
+                                   void* final_state, void* workspace, void* stream,
+                                   int64_t num_tokens, int32_t heads, int32_t num_seqs,
+                                   kda_state_dtype_t state_dtype, size_t workspace_bytes) {
+  const int64_t row = int64_t(heads) * KDA_HEAD_DIM;
+  const kda_strides_t dense{row, KDA_HEAD_DIM, row, KDA_HEAD_DIM, row,   KDA_HEAD_DIM,
+                            row, KDA_HEAD_DIM, heads, 1,          row, KDA_HEAD_DIM};
+  return forward(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, scale, initial_state,
+                 cu_seqlens, out, final_state, workspace, stream, num_tokens, heads, num_seqs,
+                 state_dtype, workspace_bytes, dense);
+}
+
+kda_status_t kda_chunk_prefill_fwd_strided(
+    const void* q, const void* k, const void* v, const void* g, const void* beta_logits,
+    const float* A_log, const float* dt_bias, float lower_bound, float scale,
+    const void* initial_state, const int32_t* cu_seqlens, void* out, void* final_state,
+    void* workspace, void* stream, int64_t num_tokens, int32_t heads, int32_t num_seqs,
+    kda_state_dtype_t state_dtype, size_t workspace_bytes, const kda_strides_t* strides) {
+  if (!strides) return KDA_ERR_INVALID_ARG;
+  return forward(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, scale, initial_state,
+                 cu_seqlens, out, final_state, workspace, stream, num_tokens, heads, num_seqs,
+                 state_dtype, workspace_bytes, *strides);
 }
 
 }  // extern "C"

@@ -163,26 +163,33 @@ __device__ __forceinline__ void load_row(Prefetch<VS>& pf, int r, const uint16_t
 
 // Fetch chunk [t0, t0 + L).  Offsets are 32-bit from uniform base pointers
 // (q/k/g/v point at token 0 of head h; v at this slice's first column).
+// Token strides (elements) of the per-token tensors.
+struct TokStrides {
+  unsigned q, k, g, v, b;
+};
+
 template <int VS>
 __device__ __forceinline__ void load_chunk(Prefetch<VS>& pf, const uint16_t* q, const uint16_t* k,
                                            const uint16_t* g, const uint16_t* v,
-                                           const uint16_t* beta, int rowstride, int H, int t0,
+                                           const uint16_t* beta, const TokStrides& ts, int t0,
                                            int L, int tq, int tid) {
   constexpr int VN = Prefetch<VS>::VN;
   const unsigned ck = 8u * (unsigned)(tid & 15), cv = (unsigned)(tid & 15) * VN;
   if (L == kC) {  // full chunk: no per-row predicates
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const unsigned off = (unsigned)(t0 + 4 * tq + r) * (unsigned)rowstride;
-      load_row<VS>(pf, r, q + (off + ck), k + (off + ck), g + (off + ck), v + (off + cv));
+      const unsigned t = (unsigned)(t0 + 4 * tq + r);
+      load_row<VS>(pf, r, q + (t * ts.q + ck), k + (t * ts.k + ck), g + (t * ts.g + ck),
+                   v + (t * ts.v + cv));
     }
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 4 * tq + r;
       if (t < L) {
-        const unsigned off = (unsigned)(t0 + t) * (unsigned)rowstride;
-        load_row<VS>(pf, r, q + (off + ck), k + (off + ck), g + (off + ck), v + (off + cv));
+        const unsigned tt = (unsigned)(t0 + t);
+        load_row<VS>(pf, r, q + (tt * ts.q + ck), k + (tt * ts.k + ck), g + (tt * ts.g + ck),
+                     v + (tt * ts.v + cv));
       } else {
         pf.q[r] = pf.k[r] = pf.g[r] = uint4{0, 0, 0, 0};
 #pragma unroll
@@ -190,7 +197,7 @@ __device__ __forceinline__ void load_chunk(Prefetch<VS>& pf, const uint16_t* q, 
       }
     }
   }
-  pf.beta = (tid < L) ? beta[(unsigned)(t0 + tid) * (unsigned)H] : uint16_t(0);
+  pf.beta = (tid < L) ? beta[(unsigned)(t0 + tid) * ts.b] : uint16_t(0);
 }
 
 // Elementwise pass of one chunk, kept in registers until the chunk's operand
@@ -323,19 +330,22 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
   const int eos = min(max(p.cu[n + 1], bos), p.T);
 
   // base pointers of token 0 for this head (and this thread's channels);
-  // per-token offsets below are 32-bit (T * H * 128 < 2^31 elements is checked on the host)
-  const int rowstride = H * kD;
-  const uint16_t* qb = p.q + (size_t)h * kD;
-  const uint16_t* kb = p.k + (size_t)h * kD;
-  const uint16_t* gb = p.g + (size_t)h * kD;
-  const uint16_t* vb = p.v + (size_t)h * kD + slice * VS;
-  const uint16_t* betab = p.beta + h;
-  uint16_t* outb = p.out + (size_t)h * kD + slice * VS;
+  // per-token offsets below are 32-bit ((T + 256) * stride < 2^31 elements is
+  // checked on the host)
+  const TokStrides ts{unsigned(p.ts_q), unsigned(p.ts_k), unsigned(p.ts_g), unsigned(p.ts_v),
+                      unsigned(p.ts_b)};
+  const unsigned ts_o = unsigned(p.ts_o);
+  const uint16_t* qb = p.q + (size_t)h * p.hs_q;
+  const uint16_t* kb = p.k + (size_t)h * p.hs_k;
+  const uint16_t* gb = p.g + (size_t)h * p.hs_g;
+  const uint16_t* vb = p.v + (size_t)h * p.hs_v + slice * VS;
+  const uint16_t* betab = p.beta + (size_t)h * p.hs_b;
+  uint16_t* outb = p.out + (size_t)h * p.hs_o + slice * VS;
 
   Prefetch<VS> pf;
   Elem<VS> el;
   if (bos < eos) {
-    load_chunk<VS>(pf, qb, kb, gb, vb, betab, rowstride, H, bos, min(kC, eos - bos), tq, tid);
+    load_chunk<VS>(pf, qb, kb, gb, vb, betab, ts, bos, min(kC, eos - bos), tq, tid);
     elementwise<VS>(el, pf, min(kC, eos - bos), tq, g4, c2, c1, lb2, p.scale, &sm.rloc[wave][ch0],
                     &sm.wtot[wave][ch0]);
   }
@@ -346,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
 
     // fetch the next chunk; its elementwise pass runs during this chunk's state part
     const int Ln = min(kC, eos - t0 - kC);  // <= 0 when this is the last chunk
-    if (Ln > 0) load_chunk<VS>(pf, qb, kb, gb, vb, betab, rowstride, H, t0 + kC, Ln, tq, tid);
+    if (Ln > 0) load_chunk<VS>(pf, qb, kb, gb, vb, betab, ts, t0 + kC, Ln, tq, tid);
 
     // ---------------- decay factors and MFMA operands ----------------
     // R: G at token 7 of this sub-chunk (relative to the sub-chunk start);
@@ -683,12 +693,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
         if (L == kC) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            ocol[(unsigned)(t0 + 16 * rt + 4 * g4 + j) * (unsigned)rowstride] = ob[st][rt][j];
+            ocol[(unsigned)(t0 + 16 * rt + 4 * g4 + j) * ts_o] = ob[st][rt][j];
         } else {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int t = 16 * rt + 4 * g4 + j;
-            if (t < L) ocol[(unsigned)(t0 + t) * (unsigned)rowstride] = ob[st][rt][j];
+            if (t < L) ocol[(unsigned)(t0 + t) * ts_o] = ob[st][rt][j];
           }
         }
       }

@@ -11,8 +11,8 @@ constexpr int kD = 128;  // head_dim (keys and values)
 constexpr float kNormEps = 1e-6f;
 
 // Everything a kernel needs for one call.  Tensor layouts are those of
-// include/kda.h: q/k/v/g/out [T, H, D] bf16, beta [T, H] bf16, state
-// [N, H, D, D] (row = key channel, column = value channel).
+// include/kda.h: q/k/v/g/out [T, H, D] bf16 rows at the strides below, beta
+// [T, H] bf16, state [N, H, D, D] (row = key channel, column = value channel).
 struct Params {
   const uint16_t* q;
   const uint16_t* k;
@@ -29,6 +29,11 @@ struct Params {
                    // null: the kernel ranks the sequences itself (pipelined kernel, N small)
   float lower_bound;
   float scale;
+  // element strides of the per-token tensors (channels contiguous): row
+  // (t, h) of q starts at q + t * ts_q + h * hs_q; beta[t, h] at
+  // beta + t * ts_b + h * hs_b.  Every (T + 256) * ts + (H - 1) * hs + 128 < 2^31.
+  int ts_q, ts_k, ts_v, ts_g, ts_b, ts_o;
+  int hs_q, hs_k, hs_v, hs_g, hs_b, hs_o;
   int T;           // tokens in q/k/v/g/out (sequence offsets are clamped to it)
   int H;
   int N;

@@ -94,8 +94,9 @@ __device__ __forceinline__ int frag(int blk, int m, int k) {
 constexpr int kRsrcWord3 = 0x00020000;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int eos, int rowstride,
                                                           int rowlen) {
-  const int bytes = eos > 0 ? ((eos - 1) * rowstride + rowlen) * 2 : 0;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+  // below 2^32 by the host's size check; formed unsigned
+  const unsigned bytes = eos > 0 ? (unsigned(eos - 1) * unsigned(rowstride) + unsigned(rowlen)) * 2u : 0u;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), kRsrcWord3);
 }
 
 template <int B>
@@ -145,35 +146,35 @@ struct RawSrc {
 // as zeros (buffer range check), so the loads need no condition.
 struct RawLoad {
   RawSrc src;
-  int rowstride, H, lane, hf;
+  int ts_q, ts_k, ts_g, ts_b, lane, hf;  // token strides (elements) of q, k, g, beta
 
   // rows for the norms, and beta
   __device__ __forceinline__ void rows(Raw& r, int t0) const {
-    const unsigned offn =
-        ((unsigned(t0) + unsigned(lane >> 2)) * unsigned(rowstride) + 32u * unsigned(lane & 3)) * 2u;
+    const unsigned tok = unsigned(t0) + unsigned(lane >> 2), c0 = 32u * unsigned(lane & 3);
+    const unsigned offk = (tok * unsigned(ts_k) + c0) * 2u, offq = (tok * unsigned(ts_q) + c0) * 2u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      r.kn[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src.k, offn + 16u * i, 0, 0));
-      r.qn[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src.qn, offn + 16u * i, 0, 0));
+      r.kn[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src.k, offk + 16u * i, 0, 0));
+      r.qn[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src.qn, offq + 16u * i, 0, 0));
     }
-    r.beta = __builtin_amdgcn_raw_buffer_load_b16(src.beta, (unsigned(t0) + unsigned(lane)) * unsigned(H) * 2u, 0, 0);
+    r.beta = __builtin_amdgcn_raw_buffer_load_b16(src.beta, (unsigned(t0) + unsigned(lane)) * unsigned(ts_b) * 2u, 0, 0);
   }
-  __device__ __forceinline__ unsigned col_off(int t0, int rr) const {
+  __device__ __forceinline__ unsigned col_off(int t0, int rr, int ts) const {
     const unsigned ch = 64u * unsigned(hf) + 4u * unsigned(lane & 15), tq = unsigned(lane >> 4);
-    return ((unsigned(t0) + 4u * tq + rr) * unsigned(rowstride) + ch) * 2u;
+    return ((unsigned(t0) + 4u * tq + rr) * unsigned(ts) + ch) * 2u;
   }
   // gate inputs
   __device__ __forceinline__ void gate(Raw& r, int t0) const {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-      r.g[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.g, col_off(t0, rr), 0, 0));
+      r.g[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.g, col_off(t0, rr, ts_g), 0, 0));
   }
   // q and k
   __device__ __forceinline__ void qk(Raw& r, int t0) const {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      r.q[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.q, col_off(t0, rr), 0, 0));
-      r.k[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.k, col_off(t0, rr), 0, 0));
+      r.q[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.q, col_off(t0, rr, ts_q), 0, 0));
+      r.k[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.k, col_off(t0, rr, ts_k), 0, 0));
     }
   }
   __device__ __forceinline__ void all(Raw& r, int t0) const {
@@ -472,7 +473,6 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   const int eos = min(max(p.cu[n + 1], bos), p.T);
   const int nc = (eos - bos + kTok - 1) / kTok;  // chunks
   const int nr = (nc + kPW - 1) / kPW;            // rounds
-  const int rowstride = H * kD;
 
   if (wave < kProdWaves) {
     // ---------------- producer waves ----------------
@@ -480,11 +480,11 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
     // waves of a chunk share a SIMD
     const int c = wave & (kPW - 1), hf = wave / kPW;
     RawSrc src;
-    src.q = rows_rsrc(p.q + size_t(h) * kD, eos, rowstride, kD);
-    src.k = rows_rsrc(p.k + size_t(h) * kD, eos, rowstride, kD);
-    src.g = rows_rsrc(p.g + size_t(h) * kD, eos, rowstride, kD);
-    src.qn = rows_rsrc(p.q + size_t(h) * kD, hf ? eos : 0, rowstride, kD);
-    src.beta = rows_rsrc(p.beta + h, hf ? 0 : eos, H, 1);
+    src.q = rows_rsrc(p.q + size_t(h) * p.hs_q, eos, p.ts_q, kD);
+    src.k = rows_rsrc(p.k + size_t(h) * p.hs_k, eos, p.ts_k, kD);
+    src.g = rows_rsrc(p.g + size_t(h) * p.hs_g, eos, p.ts_g, kD);
+    src.qn = rows_rsrc(p.q + size_t(h) * p.hs_q, hf ? eos : 0, p.ts_q, kD);
+    src.beta = rows_rsrc(p.beta + size_t(h) * p.hs_b, hf ? 0 : eos, p.ts_b, 1);
     const float eA = expf(p.A_log[h]);
     const float c1 = -kLog2e * eA;
     const float lb2 = p.lower_bound * kLog2e;
@@ -492,7 +492,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) c2[i] = c1 * p.dt_bias[h * kD + 64 * hf + 4 * (lane & 15) + i];
     __builtin_amdgcn_sched_barrier(0);  // constants first: nothing waits behind the first chunk's loads
-    const RawLoad ld{src, rowstride, H, lane, hf};
+    const RawLoad ld{src, p.ts_q, p.ts_k, p.ts_g, p.ts_b, lane, hf};
     Raw raw;
     ld.all(raw, bos + kTok * c);
     bf16* kg = sm.kg[c];
@@ -527,8 +527,8 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   // S[u][rt][j] = S[16 rt + 4 g4 + j][column of strip u]
   const int sw = wave - kProdWaves;
   const int colb = slice * VS + 16 * sw + l16;  // column of strip 0; strip u adds 16 NSW u
-  const __amdgpu_buffer_rsrc_t vsrc = rows_rsrc(p.v + size_t(h) * kD, eos, rowstride, kD);
-  const __amdgpu_buffer_rsrc_t odst = rows_rsrc(p.out + size_t(h) * kD, eos, rowstride, kD);
+  const __amdgpu_buffer_rsrc_t vsrc = rows_rsrc(p.v + size_t(h) * p.hs_v, eos, p.ts_v, kD);
+  const __amdgpu_buffer_rsrc_t odst = rows_rsrc(p.out + size_t(h) * p.hs_o, eos, p.ts_o, kD);
   const size_t sbase = (size_t(n) * H + h) * kD * kD;
   f32x4 S[SPW][8];
   if (!p.s0) {
@@ -578,7 +578,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
     for (int c = 0; c < kPW; ++c) {
       const int t0 = bos + kTok * (kPW * r + c);
 #pragma unroll
-      for (int u = 0; u < SPW; ++u) v[c][u] = load_vrow(vsrc, cstrip + 16 * NSW * u, rowstride, t0, lane);
+      for (int u = 0; u < SPW; ++u) v[c][u] = load_vrow(vsrc, cstrip + 16 * NSW * u, p.ts_v, t0, lane);
     }
   };
   // chunks of round r - 1, in order, from package buffer B = (r - 1) % 2:
@@ -642,7 +642,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
         const bf16x4 orow = tr4(&tl.o[64 * g4 + 16 * (l16 >> 2) + 4 * (l16 & 3)]);
         __builtin_amdgcn_raw_buffer_store_b64(
             __builtin_bit_cast(u32x2, orow), odst,
-            ((unsigned(t0) + unsigned(l16)) * unsigned(rowstride) + cstrip + 16 * NSW * u + 4u * g4) * 2u,
+            ((unsigned(t0) + unsigned(l16)) * unsigned(p.ts_o) + cstrip + 16 * NSW * u + 4u * g4) * 2u,
             0, 0);
         // S <- Diag(e^{G_last}) S + K'^T N in fp16 operands (kKpScale K' and
         // kNScale N; k-slots: this lane group's four tokens).  The accumulator

@@ -79,10 +79,10 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(Params p) {
   for (int t0 = bos; t0 < eos; t0 += kTB) {
     const int nt = min(kTB, eos - t0);
     for (int tt = wave; tt < nt; tt += 4) {
-      const size_t base = ((size_t)(t0 + tt) * H + h) * kD;
-      const uint32_t qp = reinterpret_cast<const uint32_t*>(p.q + base)[lane];
-      const uint32_t kp = reinterpret_cast<const uint32_t*>(p.k + base)[lane];
-      const uint32_t gp = reinterpret_cast<const uint32_t*>(p.g + base)[lane];
+      const size_t t = size_t(t0 + tt);
+      const uint32_t qp = reinterpret_cast<const uint32_t*>(p.q + t * p.ts_q + size_t(h) * p.hs_q)[lane];
+      const uint32_t kp = reinterpret_cast<const uint32_t*>(p.k + t * p.ts_k + size_t(h) * p.hs_k)[lane];
+      const uint32_t gp = reinterpret_cast<const uint32_t*>(p.g + t * p.ts_g + size_t(h) * p.hs_g)[lane];
       float q0 = bf16_lo(qp), q1 = bf16_hi(qp);
       float k0 = bf16_lo(kp), k1 = bf16_hi(kp);
       const float rq = rsqrtf(wave_sum(q0 * q0 + q1 * q1) + kNormEps) * p.scale;
@@ -100,10 +100,10 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(Params p) {
       s_a[tt][2 * lane + 1] = expf(p.lower_bound / (1.f + expf(-x1)));
       if (lane < VS / 2) {
         reinterpret_cast<uint32_t*>(&s_v[tt][0])[lane] =
-            reinterpret_cast<const uint32_t*>(p.v + base + slice * VS)[lane];
+            reinterpret_cast<const uint32_t*>(p.v + t * p.ts_v + size_t(h) * p.hs_v + slice * VS)[lane];
       }
       if (lane == 0) {
-        s_beta[tt] = 1.f / (1.f + expf(-bf16_to_f32(p.beta[(size_t)(t0 + tt) * H + h])));
+        s_beta[tt] = 1.f / (1.f + expf(-bf16_to_f32(p.beta[t * p.ts_b + size_t(h) * p.hs_b])));
         s_kq[tt] = kq;
       }
     }
@@ -152,7 +152,8 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(Params p) {
         S[i] = fmaf(k4.x, d, S[i]); S[i + 1] = fmaf(k4.y, d, S[i + 1]);
         S[i + 2] = fmaf(k4.z, d, S[i + 2]); S[i + 3] = fmaf(k4.w, d, S[i + 3]);
       }
-      if (rg == 0) p.out[((size_t)(t0 + tt) * H + h) * kD + j] = f32_to_bf16(fmaf(s_kq[tt], d, pq));
+      if (rg == 0)
+        p.out[size_t(t0 + tt) * p.ts_o + size_t(h) * p.hs_o + j] = f32_to_bf16(fmaf(s_kq[tt], d, pq));
     }
     __syncthreads();
   }

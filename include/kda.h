@@ -86,7 +86,9 @@ size_t kda_get_workspace_size(int64_t max_tokens, int32_t heads, int32_t max_seq
  *   stream         hipStream_t to queue the work on (NULL = default stream)
  *
  * q, k, v, g, beta_logits and out may be NULL when num_tokens is 0; every other
- * pointer except initial_state and workspace is required.  Size limits:
+ * pointer except initial_state and workspace is required.  q, k, v, g and out
+ * must be 16-byte aligned (the kernels read and write them with 8- and 16-byte
+ * accesses).  Size limits:
  * (num_tokens + 256) * heads * 128 < 2^31 (token rows, and rows up to 256
  * past a sequence's end that the kernels read as zeros, are addressed with
  * 32-bit byte offsets), heads <= 65536, num_seqs * heads * 8 < 2^31.
@@ -106,6 +108,50 @@ kda_status_t kda_chunk_prefill_fwd(const void* q, const void* k, const void* v, 
                                    void* final_state, void* workspace, void* stream,
                                    int64_t num_tokens, int32_t heads, int32_t num_seqs,
                                    kda_state_dtype_t state_dtype, size_t workspace_bytes);
+
+/*
+ * Element strides (counted in elements, not bytes) of the per-token tensors,
+ * for kda_chunk_prefill_fwd_strided: row (t, h) of q starts at
+ * q + t * q_token + h * q_head and holds its 128 channels contiguously; the
+ * same for k, v, g and out; beta_logits[t, h] is at beta + t * beta_token +
+ * h * beta_head.  The dense layout of kda_chunk_prefill_fwd is
+ * x_token = heads * 128, x_head = 128, beta_token = heads, beta_head = 1.
+ */
+typedef struct {
+  int64_t q_token, q_head;
+  int64_t k_token, k_head;
+  int64_t v_token, v_head;
+  int64_t g_token, g_head;
+  int64_t beta_token, beta_head;
+  int64_t out_token, out_head;
+} kda_strides_t;
+
+/*
+ * kda_chunk_prefill_fwd on strided inputs and output, so that a caller whose
+ * q, k, v, g are views into a larger projection output (or whose beta logits
+ * are a column slice) passes them without dense copies.  The wrapper listing
+ * in vLLM PR #55737's report ("Key source snippets") makes such copies because
+ * FlashKDA fixes the q/k/v/g strides (only beta may be row-strided); the
+ * report's "Risks" list counts their cost.
+ *
+ *   strides   host pointer (required), see kda_strides_t.  For q, k, v, g and
+ *             out, both strides must be non-negative multiples of 8 elements;
+ *             beta's strides non-negative.  For each tensor,
+ *             (num_tokens + 256) * x_token + (heads - 1) * x_head + 128 < 2^31
+ *             (the same 32-bit addressing as the dense call).  Rows of out
+ *             that overlap give undefined results.
+ *
+ * Every other argument, the pointer rules, the limits and the guarantees are
+ * those of kda_chunk_prefill_fwd, whose results it reproduces bit for bit for
+ * the same values.  q, k, v, g and out must be 16-byte aligned (as in the
+ * dense call).
+ */
+kda_status_t kda_chunk_prefill_fwd_strided(
+    const void* q, const void* k, const void* v, const void* g, const void* beta_logits,
+    const float* A_log, const float* dt_bias, float lower_bound, float scale,
+    const void* initial_state, const int32_t* cu_seqlens, void* out, void* final_state,
+    void* workspace, void* stream, int64_t num_tokens, int32_t heads, int32_t num_seqs,
+    kda_state_dtype_t state_dtype, size_t workspace_bytes, const kda_strides_t* strides);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* kda_status_string(kda_status_t status);

@@ -31,8 +31,8 @@ def test_library_exports_every_declared_symbol():
     lib = kda.load_library()
     names = _declared_functions()
     assert set(names) == {"kda_get_workspace_size", "kda_chunk_prefill_fwd",
-                          "kda_status_string", "kda_last_hip_error", "kda_debug_set_vsplit",
-                          "kda_debug_set_kernel"}
+                          "kda_chunk_prefill_fwd_strided", "kda_status_string",
+                          "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/kda.h but not exported"
 
@@ -139,3 +139,58 @@ def test_one_hip_runtime_in_the_process():
     maps = open("/proc/self/maps").read().splitlines()
     libs = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
     assert len(libs) == 1, f"more than one HIP runtime mapped: {sorted(libs)}"
+
+
+def test_misaligned_dense_tensor_rejected():
+    # q, k, v, g and out are read and written with 8- and 16-byte accesses
+    for name in ("q", "k", "v", "g", "out"):
+        assert _call(**{name: ctypes.c_void_p(0x1008)}) == INVALID
+    assert _call(beta=ctypes.c_void_p(0x1001)) == INVALID
+
+
+def _dense_strides(H):
+    row = H * 128
+    return kda._Strides(row, 128, row, 128, row, 128, row, 128, H, 1, row, 128)
+
+
+def _call_strided(strides, **over):
+    """kda_chunk_prefill_fwd_strided through ctypes; defaults as _call."""
+    lib = kda.load_library()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE,
+             lb=-5.0, scale=128 ** -0.5, s0=None, cu=FAKE, out=FAKE, sT=FAKE, ws=FAKE,
+             stream=None, T=16384, H=16, N=8, sdt=0, wsb=1 << 20)
+    a.update(over)
+    return lib.kda_chunk_prefill_fwd_strided(
+        a["q"], a["k"], a["v"], a["g"], a["beta"], a["A_log"], a["dt_bias"], a["lb"],
+        a["scale"], a["s0"], a["cu"], a["out"], a["sT"], a["ws"], a["stream"], a["T"], a["H"],
+        a["N"], a["sdt"], a["wsb"], None if strides is None else ctypes.byref(strides))
+
+
+def test_strided_entry_checks():
+    assert _call_strided(None) == INVALID
+    # the checks run in the dense call's order: a bad lower_bound with good
+    # strides is UNSUPPORTED, exactly as for the dense entry
+    assert _call_strided(_dense_strides(16), lb=-7.0) == UNSUPPORTED
+    assert _call_strided(_dense_strides(16), wsb=0) == WS_SMALL
+    for field, value in [("q_token", 16 * 128 + 4), ("k_head", 132), ("v_token", -8),
+                         ("g_head", 3), ("out_token", 2 ** 20), ("beta_token", -1),
+                         ("beta_head", 2 ** 30)]:
+        st = _dense_strides(16)
+        setattr(st, field, value)
+        assert _call_strided(st) == INVALID, field
+    # (T + 256) * token + (H - 1) * head + 128 must stay below 2^31 elements
+    st = _dense_strides(16)
+    st.q_token = 16 * 128 * 128
+    assert _call_strided(st, T=16384) == INVALID
+    st.q_token = 16 * 128 * 4
+    assert _call_strided(st, T=16384, lb=-7.0) == UNSUPPORTED  # strides accepted
+
+
+def test_python_binding_strided_views_keep_channel_contiguity():
+    torch = pytest.importorskip("torch")
+    T, H = 4, 2
+    bf = torch.bfloat16
+    big = torch.zeros(T, H, 256, dtype=bf)
+    with pytest.raises((ValueError, TypeError)):
+        # channels not contiguous (stride 2): rejected before anything else
+        kda._check(big[..., ::2], "q", bf, (T, H, 128), strided=True)
