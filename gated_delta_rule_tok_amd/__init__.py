@@ -106,8 +106,9 @@ def kda_last_hip_error() -> str:
 
 
 def kda_debug_set_kernel(k: int) -> int:
-    """Test hook: 0 pipelined 16-token kernel (default), 1 64-token kernel, 2
-    token-serial kernel."""
+    """Test hook: 0 automatic (default), 1 64-token kernel, 2 token-serial
+    kernel, 3 token-serial kernel with decode staging, 4 pipelined 16-token
+    kernel (where it applies)."""
     prev = load_library().kda_debug_set_kernel(int(k))
     if prev < 0:
         raise ValueError(f"invalid kernel selector {k}")

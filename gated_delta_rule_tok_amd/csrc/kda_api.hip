@@ -92,7 +92,9 @@ const char* kda_status_string(kda_status_t status) {
 const char* kda_last_hip_error(void) { return t_last_hip_error; }
 
 int kda_debug_set_kernel(int k) {
-  if (k < 0 || k > 2) return -1;  // 0 pipelined 16-token, 1 64-token chunk, 2 token-serial
+  // 0 automatic, 1 64-token chunk, 2 token-serial, 3 token-serial decode
+  // staging (4 tokens), 4 pipelined 16-token
+  if (k < 0 || k > 4) return -1;
   return g_kernel_override.exchange(k);
 }
 
@@ -185,19 +187,25 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   hipStream_t st = static_cast<hipStream_t>(stream);
   // the pipelined kernel takes lower_bound >= -5 and slices of <= 64 value
   // columns; anything else (or the test override) goes to the 64-token kernel
-  int kernel = g_kernel_override.load(std::memory_order_relaxed);
+  const int override = g_kernel_override.load(std::memory_order_relaxed);
+  int kernel = override == 4 ? 0 : override;
+  // decode-sized calls (at most kDecodeTokensPerSeq tokens per sequence on
+  // average): the token-serial kernel streams each state once with little
+  // LDS per workgroup; the chunked kernels' machinery does not pay off there
+  if (override == 0 && num_tokens <= kda::kDecodeTokensPerSeq * int64_t(num_seqs)) kernel = 3;
   if (kernel == 0 && lower_bound < kda::kPipeLowerBoundMin) kernel = 1;
   if (kernel == 0 && p.vsplit == 1) p.vsplit = forced > 0 ? 1 : 2;
   if (kernel == 0 && p.vsplit == 1) kernel = 1;
   // the sequence order table (longest first): the pipelined kernel ranks a
-  // few sequences itself, everything else reads the table
-  if (kernel == 0 && num_seqs <= kda::kInlineRankMax) {
+  // few sequences itself, the decode path takes them in index order, the
+  // others read the table
+  if ((kernel == 0 && num_seqs <= kda::kInlineRankMax) || kernel == 3) {
     p.order = nullptr;
   } else if (hipError_t e = kda::launch_plan(p, st); e != hipSuccess) {
     return hip_failure(e, "plan launch");
   }
-  if (kernel == 2) {
-    if (hipError_t e = kda::launch_recurrent(p, st); e != hipSuccess)
+  if (kernel == 2 || kernel == 3) {
+    if (hipError_t e = kda::launch_recurrent(p, st, kernel == 3); e != hipSuccess)
       return hip_failure(e, "token-serial kernel launch");
   } else if (kernel == 1) {
     if (hipError_t e = kda::launch_chunk(p, st); e != hipSuccess)

@@ -25,7 +25,6 @@ namespace kda {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTB = 32;  // tokens staged in LDS per step
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -33,7 +32,10 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <int VS>
+// kTB: tokens staged in LDS per step (32 for prefill; 4 for decode-sized
+// sequences, which keeps the LDS block small so more workgroups stream their
+// state at once)
+template <int VS, int kTB>
 __global__ __launch_bounds__(kThreads) void recurrent_kernel(Params p) {
   constexpr int CW = VS / 4;   // value columns per wave
   constexpr int RG = 64 / CW;  // row groups per wave
@@ -51,7 +53,8 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(Params p) {
   const int slice = blockIdx.x % p.vsplit;
   const int rest = blockIdx.x / p.vsplit;
   const int h = rest % p.H;
-  const int n = p.order[rest / p.H];
+  // sequence: from the order table, or the rank itself when there is none
+  const int n = p.order ? p.order[rest / p.H] : rest / p.H;
   const int H = p.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane % CW, rg = lane / CW;
@@ -168,13 +171,19 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(Params p) {
 
 }  // namespace
 
-hipError_t launch_recurrent(const Params& p, hipStream_t stream) {
+hipError_t launch_recurrent(const Params& p, hipStream_t stream, bool decode) {
   const void* fn = nullptr;
   switch (kD / p.vsplit) {
-    case 128: fn = reinterpret_cast<const void*>(&recurrent_kernel<128>); break;
-    case 64: fn = reinterpret_cast<const void*>(&recurrent_kernel<64>); break;
-    case 32: fn = reinterpret_cast<const void*>(&recurrent_kernel<32>); break;
-    case 16: fn = reinterpret_cast<const void*>(&recurrent_kernel<16>); break;
+#define KDA_RECURRENT_CASE(VS)                                                                \
+  case VS:                                                                                    \
+    fn = decode ? reinterpret_cast<const void*>(&recurrent_kernel<VS, 4>)                     \
+                : reinterpret_cast<const void*>(&recurrent_kernel<VS, 32>);                   \
+    break;
+    KDA_RECURRENT_CASE(128)
+    KDA_RECURRENT_CASE(64)
+    KDA_RECURRENT_CASE(32)
+    KDA_RECURRENT_CASE(16)
+#undef KDA_RECURRENT_CASE
     default: return hipErrorInvalidValue;
   }
   Params arg = p;

@@ -175,14 +175,18 @@ const char* kda_last_hip_error(void);
 int kda_debug_set_vsplit(int s);
 
 /*
- * Test hook: choose the kernel family -- 0 (default): the pipelined 16-token
+ * Test hook: choose the kernel family -- 0 (default): automatic: calls with
+ * at most 2 tokens per sequence on average (decode-sized) take the
+ * token-serial kernel with 4-token staging; otherwise the pipelined 16-token
  * chunk kernel for lower_bound >= -5 with the value dimension split at least
- * in two (a forced split of 1 and lower_bound < -5 use the 64-token kernel);
- * 1: the 64-token chunk kernel (WY/UT with a blocked forward substitution
- * over the 64x64 triangle); 2: the token-serial fp32 kernel, an independent
- * GPU implementation of the same recurrence used to cross-check the chunked
- * ones.  Process-wide.  Returns the previous setting, or -1 (unchanged) for
- * an invalid value.
+ * in two, else the 64-token kernel.  1: the 64-token chunk kernel (WY/UT with
+ * a blocked forward substitution over the 64x64 triangle); 2: the
+ * token-serial fp32 kernel (32-token staging), an independent GPU
+ * implementation of the same recurrence used to cross-check the chunked ones;
+ * 3: the token-serial kernel with 4-token staging; 4: the pipelined kernel
+ * whatever the call's size (falling back as in 0 where it does not apply).
+ * Process-wide.  Returns the previous setting, or -1 (unchanged) for an
+ * invalid value.
  */
 int kda_debug_set_kernel(int k);
 

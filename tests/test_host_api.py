@@ -194,3 +194,12 @@ def test_python_binding_strided_views_keep_channel_contiguity():
     with pytest.raises((ValueError, TypeError)):
         # channels not contiguous (stride 2): rejected before anything else
         kda._check(big[..., ::2], "q", bf, (T, H, 128), strided=True)
+
+
+def test_debug_kernel_hook():
+    lib = kda.load_library()
+    for k in (1, 2, 3, 4, 0):
+        assert lib.kda_debug_set_kernel(k) >= 0
+    assert lib.kda_debug_set_kernel(5) == -1
+    assert lib.kda_debug_set_kernel(-1) == -1
+    assert lib.kda_debug_set_kernel(0) == 0

@@ -42,13 +42,13 @@ def test_config_parity(idx):
     assert_parity(x, out, fin, oref, fref, label=f"config {idx}")
 
 
-@pytest.mark.parametrize("kernel,splits", [(0, (2, 4, 8)), (1, (1, 2, 4, 8))])
+@pytest.mark.parametrize("kernel,splits", [(4, (2, 4, 8)), (1, (1, 2, 4, 8)), (3, (1, 2, 4, 8))])
 @pytest.mark.parametrize("idx", [3, 0, 1])
 def test_vsplit_bit_identical(idx, kernel, splits):
     """Splitting the value dimension over workgroups changes nothing, bit for
     bit: each value column's arithmetic is the same whatever the split.  The
-    pipelined kernel (0) takes splits of 2 and more; the 64-token kernel (1)
-    also runs unsplit."""
+    pipelined kernel (4) takes splits of 2 and more; the 64-token kernel (1)
+    and the token-serial decode path (3) also run unsplit."""
     import torch
     import gated_delta_rule_tok_amd as kda
     x, _ = _config(idx)
@@ -258,3 +258,28 @@ def test_token_serial_kernel_parity(idx):
     finally:
         kda.kda_debug_set_kernel(prev)
     assert_parity(x, out, fin, oref, fref, label=f"token-serial config {idx}")
+
+
+@pytest.mark.parametrize("lengths,state,lb", [
+    ([1] * 96, "fp32", -5.0),                 # decode: one token per sequence
+    ([2, 3, 0, 2, 1] * 12, "bf16", -5.5),     # speculative-decode-sized, empty ones too
+    ([1] * 40 + [30], "fp32", -1.0),          # decode-sized on average, one longer sequence
+    ([4, 3, 4, 1] * 10, "fp32", -5.0),        # above the decode threshold: pipelined
+])
+def test_decode_sized_calls(lengths, state, lb):
+    """At most 2 tokens per sequence on average: the automatic choice is the
+    token-serial kernel with decode staging; both it and the pipelined kernel
+    match the oracle from a nonzero initial state, and so does the automatic
+    choice above the threshold."""
+    import gated_delta_rule_tok_amd as kda
+    x = KI.make_inputs(lengths, 4, seed=43, init_state=state, lower_bound=lb)
+    print(f"[case] decode-sized N={x.N} T={x.T} state={state} lb={lb}", flush=True)
+    oref, fref = run_oracle(x)
+    d = to_device(x)
+    for kernel in (0, 4):
+        prev = kda.kda_debug_set_kernel(kernel)
+        try:
+            out, fin = run_gpu(x, d)
+        finally:
+            kda.kda_debug_set_kernel(prev)
+        assert_parity(x, out, fin, oref, fref, label=f"decode-sized kernel {kernel}")

@@ -47,7 +47,7 @@ def _strided_views(d, layout):
     return sd, out, obuf
 
 
-@pytest.mark.parametrize("kernel", [0, 1, 2])
+@pytest.mark.parametrize("kernel", [4, 1, 2, 3])
 @pytest.mark.parametrize("layout", ["fused_rows", "per_head"])
 def test_strided_matches_dense_bitwise(kernel, layout):
     import torch
