@@ -190,8 +190,8 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   const int override = g_kernel_override.load(std::memory_order_relaxed);
   int kernel = override == 4 ? 0 : override;
   // decode-sized calls (at most kDecodeTokensPerSeq tokens per sequence on
-  // average): the token-serial kernel streams each state once with little
-  // LDS per workgroup; the chunked kernels' machinery does not pay off there
+  // average): the decode kernel streams each state once with 16-byte
+  // accesses; the chunked kernels' machinery does not pay off there
   if (override == 0 && num_tokens <= kda::kDecodeTokensPerSeq * int64_t(num_seqs)) kernel = 3;
   if (kernel == 0 && lower_bound < kda::kPipeLowerBoundMin) kernel = 1;
   if (kernel == 0 && p.vsplit == 1) p.vsplit = forced > 0 ? 1 : 2;

@@ -65,9 +65,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 hipError_t launch_plan(const Params& p, hipStream_t stream);
 
 // Token-serial fp32 recurrence, one workgroup per (sequence, head, V-slice).
-// decode: stage 4 tokens at a time instead of 32 (smaller LDS block, more
-// workgroups in flight; meant for sequences of a few tokens).  p.order may be
-// null (sequences taken in index order).
+// decode: the decode kernel (16-byte state accesses, 4 tokens staged at a
+// time; slices of 16 or 32 columns stage 4 tokens in the 4-byte kernel), for
+// sequences of a few tokens, giving the same bits.  p.order may be null
+// (sequences taken in index order).
 hipError_t launch_recurrent(const Params& p, hipStream_t stream, bool decode);
 
 // Chunked (64-token WY/UT) forward with bf16 MFMA, one workgroup per
@@ -83,7 +84,7 @@ hipError_t launch_chunk(const Params& p, hipStream_t stream);
 constexpr float kPipeLowerBoundMin = -5.0f;
 // Calls with at most this many tokens per sequence on average go to the
 // token-serial kernel with decode staging.
-constexpr int kDecodeTokensPerSeq = 2;
+constexpr int kDecodeTokensPerSeq = 8;
 constexpr int kInlineRankMax = 16;
 hipError_t launch_pipe(const Params& p, hipStream_t stream);
 

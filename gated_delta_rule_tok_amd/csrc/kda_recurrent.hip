@@ -169,21 +169,183 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(Params p) {
   }
 }
 
+// The same recurrence for decode-sized calls, with 16-byte state accesses:
+// wave w owns value columns [w CW, (w + 1) CW) of the slice (CW = VS / 4) and
+// lane l owns the four columns 4 (l % C4) .. + 3 (C4 = CW / 4 quads) of the R
+// consecutive key rows of row group l / C4.  The per-column arithmetic, and the
+// order of every sum, are those of recurrent_kernel (8-row sequential groups,
+// then a pairwise tree over the 16 group indices, low bits first), so both
+// kernels give the same bits.  Tokens are staged 4 at a time.
+template <int VS>
+__global__ __launch_bounds__(kThreads) void decode_kernel(Params p) {
+  constexpr int kTB = 4;
+  constexpr int CW = VS / 4;    // value columns per wave
+  constexpr int C4 = CW / 4;    // column quads per wave
+  constexpr int RG = 64 / C4;   // row groups
+  constexpr int R = kD / RG;    // key rows per lane
+  constexpr int GL = R / 8;     // 8-row reduction groups per lane
+  static_assert(R % 8 == 0, "rows per lane must be a multiple of 8");
+
+  __shared__ float s_q[kTB][kD];
+  __shared__ float s_k[kTB][kD];
+  __shared__ float s_a[kTB][kD];
+  __shared__ uint16_t s_v[kTB][VS];
+  __shared__ float s_beta[kTB];
+  __shared__ float s_kq[kTB];
+
+  const int slice = blockIdx.x % p.vsplit;
+  const int rest = blockIdx.x / p.vsplit;
+  const int h = rest % p.H;
+  const int n = p.order ? p.order[rest / p.H] : rest / p.H;
+  const int H = p.H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c4 = lane % C4, rg = lane / C4;
+  const int jl = wave * CW + 4 * c4;  // first of this lane's columns inside the slice
+  const int j = slice * VS + jl;      // ... as a value channel
+  const int r0 = rg * R;              // first key row
+
+  float4 S[R];
+  const size_t sbase = ((size_t)n * H + h) * kD * kD;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const size_t idx = sbase + (size_t)(r0 + i) * kD + j;
+    if (!p.s0) {
+      S[i] = float4{0.f, 0.f, 0.f, 0.f};
+    } else if (p.state_bf16) {
+      const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.s0) + idx);
+      S[i] = float4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+    } else {
+      S[i] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.s0) + idx);
+    }
+  }
+
+  const float eA = expf(p.A_log[h]);
+  const float dtb0 = p.dt_bias[h * kD + 2 * lane];
+  const float dtb1 = p.dt_bias[h * kD + 2 * lane + 1];
+  const int bos = min(max(p.cu[n], 0), p.T);
+  const int eos = min(max(p.cu[n + 1], bos), p.T);
+
+  for (int t0 = bos; t0 < eos; t0 += kTB) {
+    const int nt = min(kTB, eos - t0);
+    for (int tt = wave; tt < nt; tt += 4) {
+      const size_t t = size_t(t0 + tt);
+      const uint32_t qp = reinterpret_cast<const uint32_t*>(p.q + t * p.ts_q + size_t(h) * p.hs_q)[lane];
+      const uint32_t kp = reinterpret_cast<const uint32_t*>(p.k + t * p.ts_k + size_t(h) * p.hs_k)[lane];
+      const uint32_t gp = reinterpret_cast<const uint32_t*>(p.g + t * p.ts_g + size_t(h) * p.hs_g)[lane];
+      float q0 = bf16_lo(qp), q1 = bf16_hi(qp);
+      float k0 = bf16_lo(kp), k1 = bf16_hi(kp);
+      const float rq = rsqrtf(wave_sum(q0 * q0 + q1 * q1) + kNormEps) * p.scale;
+      const float rk = rsqrtf(wave_sum(k0 * k0 + k1 * k1) + kNormEps);
+      q0 *= rq; q1 *= rq;
+      k0 *= rk; k1 *= rk;
+      const float kq = wave_sum(q0 * k0 + q1 * k1);
+      const float x0 = eA * (bf16_lo(gp) + dtb0);
+      const float x1 = eA * (bf16_hi(gp) + dtb1);
+      s_q[tt][2 * lane] = q0;
+      s_q[tt][2 * lane + 1] = q1;
+      s_k[tt][2 * lane] = k0;
+      s_k[tt][2 * lane + 1] = k1;
+      s_a[tt][2 * lane] = expf(p.lower_bound / (1.f + expf(-x0)));
+      s_a[tt][2 * lane + 1] = expf(p.lower_bound / (1.f + expf(-x1)));
+      if (lane < VS / 2) {
+        reinterpret_cast<uint32_t*>(&s_v[tt][0])[lane] =
+            reinterpret_cast<const uint32_t*>(p.v + t * p.ts_v + size_t(h) * p.hs_v + slice * VS)[lane];
+      }
+      if (lane == 0) {
+        s_beta[tt] = 1.f / (1.f + expf(-bf16_to_f32(p.beta[t * p.ts_b + size_t(h) * p.hs_b])));
+        s_kq[tt] = kq;
+      }
+    }
+    __syncthreads();
+
+    for (int tt = 0; tt < nt; ++tt) {
+      float4 gk[GL], gq[GL];
+#pragma unroll
+      for (int gi = 0; gi < GL; ++gi) {
+        float4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = gi * 8; i < gi * 8 + 8; ++i) {
+          const float a = s_a[tt][r0 + i], kk = s_k[tt][r0 + i], qq = s_q[tt][r0 + i];
+          S[i].x *= a; S[i].y *= a; S[i].z *= a; S[i].w *= a;
+          ak.x = fmaf(S[i].x, kk, ak.x); ak.y = fmaf(S[i].y, kk, ak.y);
+          ak.z = fmaf(S[i].z, kk, ak.z); ak.w = fmaf(S[i].w, kk, ak.w);
+          aq.x = fmaf(S[i].x, qq, aq.x); aq.y = fmaf(S[i].y, qq, aq.y);
+          aq.z = fmaf(S[i].z, qq, aq.z); aq.w = fmaf(S[i].w, qq, aq.w);
+        }
+        gk[gi] = ak;
+        gq[gi] = aq;
+      }
+#pragma unroll
+      for (int w = 1; w < GL; w *= 2)
+#pragma unroll
+        for (int gi = 0; gi < GL; gi += 2 * w) {
+          gk[gi].x += gk[gi + w].x; gk[gi].y += gk[gi + w].y;
+          gk[gi].z += gk[gi + w].z; gk[gi].w += gk[gi + w].w;
+          gq[gi].x += gq[gi + w].x; gq[gi].y += gq[gi + w].y;
+          gq[gi].z += gq[gi + w].z; gq[gi].w += gq[gi + w].w;
+        }
+      float4 pk = gk[0], pq = gq[0];
+#pragma unroll
+      for (int m = C4; m < 64; m <<= 1) {
+        pk.x += __shfl_xor(pk.x, m, 64); pk.y += __shfl_xor(pk.y, m, 64);
+        pk.z += __shfl_xor(pk.z, m, 64); pk.w += __shfl_xor(pk.w, m, 64);
+        pq.x += __shfl_xor(pq.x, m, 64); pq.y += __shfl_xor(pq.y, m, 64);
+        pq.z += __shfl_xor(pq.z, m, 64); pq.w += __shfl_xor(pq.w, m, 64);
+      }
+      const float b = s_beta[tt];
+      const float4 d = {b * (bf16_to_f32(s_v[tt][jl]) - pk.x), b * (bf16_to_f32(s_v[tt][jl + 1]) - pk.y),
+                        b * (bf16_to_f32(s_v[tt][jl + 2]) - pk.z), b * (bf16_to_f32(s_v[tt][jl + 3]) - pk.w)};
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const float kk = s_k[tt][r0 + i];
+        S[i].x = fmaf(kk, d.x, S[i].x); S[i].y = fmaf(kk, d.y, S[i].y);
+        S[i].z = fmaf(kk, d.z, S[i].z); S[i].w = fmaf(kk, d.w, S[i].w);
+      }
+      if (rg == 0) {
+        const float kq = s_kq[tt];
+        const uint2 o = {pack_bf16x2(fmaf(kq, d.x, pq.x), fmaf(kq, d.y, pq.y)),
+                         pack_bf16x2(fmaf(kq, d.z, pq.z), fmaf(kq, d.w, pq.w))};
+        *reinterpret_cast<uint2*>(p.out + size_t(t0 + tt) * p.ts_o + size_t(h) * p.hs_o + j) = o;
+      }
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const size_t idx = sbase + (size_t)(r0 + i) * kD + j;
+    if (p.state_bf16) {
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.sT) + idx) =
+          uint2{pack_bf16x2(S[i].x, S[i].y), pack_bf16x2(S[i].z, S[i].w)};
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(p.sT) + idx) = S[i];
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_recurrent(const Params& p, hipStream_t stream, bool decode) {
   const void* fn = nullptr;
   switch (kD / p.vsplit) {
-#define KDA_RECURRENT_CASE(VS)                                                                \
-  case VS:                                                                                    \
-    fn = decode ? reinterpret_cast<const void*>(&recurrent_kernel<VS, 4>)                     \
-                : reinterpret_cast<const void*>(&recurrent_kernel<VS, 32>);                   \
-    break;
-    KDA_RECURRENT_CASE(128)
-    KDA_RECURRENT_CASE(64)
-    KDA_RECURRENT_CASE(32)
-    KDA_RECURRENT_CASE(16)
-#undef KDA_RECURRENT_CASE
+    // decode staging: 16-byte state accesses where a wave's columns hold
+    // whole 8-row groups per lane (slices of 64 or 128 columns)
+    case 128:
+      fn = decode ? reinterpret_cast<const void*>(&decode_kernel<128>)
+                  : reinterpret_cast<const void*>(&recurrent_kernel<128, 32>);
+      break;
+    case 64:
+      fn = decode ? reinterpret_cast<const void*>(&decode_kernel<64>)
+                  : reinterpret_cast<const void*>(&recurrent_kernel<64, 32>);
+      break;
+    case 32:
+      fn = decode ? reinterpret_cast<const void*>(&recurrent_kernel<32, 4>)
+                  : reinterpret_cast<const void*>(&recurrent_kernel<32, 32>);
+      break;
+    case 16:
+      fn = decode ? reinterpret_cast<const void*>(&recurrent_kernel<16, 4>)
+                  : reinterpret_cast<const void*>(&recurrent_kernel<16, 32>);
+      break;
     default: return hipErrorInvalidValue;
   }
   Params arg = p;

@@ -176,7 +176,7 @@ int kda_debug_set_vsplit(int s);
 
 /*
  * Test hook: choose the kernel family -- 0 (default): automatic: calls with
- * at most 2 tokens per sequence on average (decode-sized) take the
+ * at most 8 tokens per sequence on average (decode-sized) take the
  * token-serial kernel with 4-token staging; otherwise the pipelined 16-token
  * chunk kernel for lower_bound >= -5 with the value dimension split at least
  * in two, else the 64-token kernel.  1: the 64-token chunk kernel (WY/UT with

@@ -264,13 +264,14 @@ def test_token_serial_kernel_parity(idx):
     ([1] * 96, "fp32", -5.0),                 # decode: one token per sequence
     ([2, 3, 0, 2, 1] * 12, "bf16", -5.5),     # speculative-decode-sized, empty ones too
     ([1] * 40 + [30], "fp32", -1.0),          # decode-sized on average, one longer sequence
-    ([4, 3, 4, 1] * 10, "fp32", -5.0),        # above the decode threshold: pipelined
+    ([4, 3, 8, 1] * 10, "fp32", -5.0),        # multi-token decode steps
+    ([12, 9, 11] * 10, "fp32", -5.0),         # above the decode threshold: pipelined
 ])
 def test_decode_sized_calls(lengths, state, lb):
-    """At most 2 tokens per sequence on average: the automatic choice is the
-    token-serial kernel with decode staging; both it and the pipelined kernel
-    match the oracle from a nonzero initial state, and so does the automatic
-    choice above the threshold."""
+    """At most 8 tokens per sequence on average: the automatic choice is the
+    decode kernel (token-serial with 16-byte state accesses); both it and the
+    pipelined kernel match the oracle from a nonzero initial state, and so does
+    the automatic choice above the threshold."""
     import gated_delta_rule_tok_amd as kda
     x = KI.make_inputs(lengths, 4, seed=43, init_state=state, lower_bound=lb)
     print(f"[case] decode-sized N={x.N} T={x.T} state={state} lb={lb}", flush=True)
