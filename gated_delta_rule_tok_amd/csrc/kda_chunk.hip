@@ -280,11 +280,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
   const int tq = tid >> 4, co = tid & 15;     // elementwise coordinates (g4 = tq % 4)
   const int ch0 = 8 * co;
 
-  // workgroup -> (sequence rank, head, slice); consecutive work items (the
-  // slices of one head) are kept on one XCD so they share q/k/g in its L2
-  int b = blockIdx.x;
-  const int G = gridDim.x;
-  if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
+  // workgroup -> (sequence rank, head, slice): ranks in order across the XCDs,
+  // the slices of one head on one XCD (sharing q/k/g in its L2)
+  const int b = work_item(blockIdx.x, gridDim.x, p.vsplit);
   const int slice = b % p.vsplit;
   const int rest = b / p.vsplit;
   const int h = rest % p.H;

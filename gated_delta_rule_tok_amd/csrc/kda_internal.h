@@ -59,6 +59,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
 }
 
+// Workgroup index B of a grid of G -> work item b = rank * s + slice (s value
+// slices per (sequence rank, head) item).  Workgroup B runs on XCD B mod 8, so
+// items are handed out in rank order across the 8 XCDs (ranked, longest-first
+// work spreads evenly over them) and the s slices of one item sit on one XCD,
+// 8 workgroup indices apart, sharing q/k/g in its L2.  Identity when G is not
+// a multiple of 8 s.
+__device__ __forceinline__ int work_item(int B, int G, int s) {
+  if (G % (8 * s)) return B;
+  const int xcd = B & 7, k = B >> 3;
+  return ((k / s) * 8 + xcd) * s + k % s;
+}
+
 // ---- launch entry points (one per kernel family) -----------------------------
 
 // Sequence order, longest first (ties by index), into p.order.  One launch.

@@ -431,11 +431,9 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
 
-  // workgroup -> (sequence rank, head, slice); the slices of one head stay on
-  // one XCD so they share q/k/g in its L2
-  int b = blockIdx.x;
-  const int G = gridDim.x;
-  if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
+  // workgroup -> (sequence rank, head, slice): ranks in order across the XCDs,
+  // the slices of one head on one XCD (sharing q/k/g in its L2)
+  const int b = work_item(blockIdx.x, gridDim.x, p.vsplit);
   const int slice = b % p.vsplit;
   const int rest = b / p.vsplit;
   const int h = rest % p.H;
