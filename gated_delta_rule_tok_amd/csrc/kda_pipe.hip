@@ -15,18 +15,22 @@
 //   S <- Diag(e^{G_last}) S + (e^{G_last - G} k)^T N
 //
 // Work split.  One workgroup per (sequence, head, value slice).  Eight
-// "producer" waves build the packages of a round of four 16-token chunks in
-// LDS, two per chunk (one per 64-channel half): first the norms, the gate,
-// the cumulative decay and the decayed operands of their channels, then,
-// after a workgroup barrier, one forms the 16x16 products A, A^T and the
-// inverse (I + A)^-1, the other M.  None of it depends on the state.  The
+// "producer" waves build the packages of four 16-token chunk slots in LDS, two
+// per chunk (one per 64-channel half): first the norms, the gate, the
+// cumulative decay and the decayed operands of their channels, then, once the
+// other half's operands are in LDS, one forms the 16x16 products A, A^T and
+// the inverse (I + A)^-1, the other M.  None of it depends on the state.  The
 // remaining waves ("state waves", one or two 16-column strips of the value
-// slice each) walk the chunks of the previous round in order, keeping their
-// strip of S (128 x 16 fp32) in registers, and apply the three state
-// contractions and the output: three chunks before the producers' mid-round
-// barrier, one after.  Packages are double-buffered per round; a second
-// barrier ends each round.  Each SIMD runs the two VALU-heavy producer waves
-// of one chunk and one MFMA-heavy state wave.
+// slice each) walk the chunks in order, keeping their strip of S (128 x 16
+// fp32) in registers, and apply the three state contractions and the output.
+// There is no workgroup barrier in the main loops: each chunk slot has two
+// package buffers (alternate rounds of four chunks) and LDS flags -- producer
+// halves that formed their operands, the round each producer half last
+// finished per buffer, the rounds each state wave is done with -- so every
+// wave waits only for the package or buffer it needs next, and the serial
+// state chain, the inverse's latency chain and the next round's operand work
+// overlap on each SIMD (each runs the two VALU-heavy producer waves of one
+// chunk slot and one MFMA-heavy state wave).
 //
 // Norms.  k is normalised before it enters any product (k~ = k / ||k||, the
 // norm from a dot-product pass over the row); q's norm is applied after the
@@ -61,7 +65,7 @@ constexpr int kTok = 16;  // tokens per chunk
 constexpr int kPW = 4;    // chunks per round
 constexpr int kPH = 2;    // producer waves per chunk (64-channel halves)
 constexpr int kProdWaves = kPW * kPH;
-constexpr int kEarly = 3;  // chunks the state waves apply before the producers' mid-round barrier
+constexpr int kSpinMax = 1 << 22;  // polls before a wait gives up (a safety bound, never reached)
 constexpr float kKpScale = 16.f;     // K' enters the fp16 state update times this
 constexpr float kNScale = 0.0625f;   // ... and N times this (exact inverse)
 
@@ -104,6 +108,24 @@ struct BufIdx {
   static constexpr int value = B;
 };
 
+// LDS counters of one workgroup.  A wave's LDS operations complete in order
+// and the release below also waits for them, so a wave that observes a count
+// (acquire) sees every package write made before the matching increments.
+__device__ __forceinline__ void arrive(int* ctr, int lane) {
+  if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// Wait until *ctr >= target.  Every count a wave waits for is produced by
+// waves of the same workgroup that do not wait, directly or through others,
+// for the waiting wave, so the wait ends; the poll bound only keeps a broken
+// count from holding the device.
+__device__ __forceinline__ void wait_count(const int* ctr, int target) {
+#pragma unroll 1
+  for (int it = 0; it < kSpinMax; ++it) {
+    if (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 // One chunk's package: written by the chunk's two producer waves, read by
 // the state waves.
 struct Pack {
@@ -118,6 +140,7 @@ struct Pack {
   float gam[128];        // e^{G_last}
 };
 static_assert(sizeof(Pack::gam) >= sizeof(int) * (kInlineRankMax + 1), "rank scratch fits in gam");
+static_assert(sizeof(Pack) % 16 == 0, "packages stay 16-byte aligned");
 
 // Raw inputs of one chunk for one producer lane of channel half hf: tokens
 // 4 tq + rr (rr = 0..3) of channels 64 hf + 4 cg .. + 3 (cg = lane % 16,
@@ -391,7 +414,6 @@ __device__ __forceinline__ void produce_m(Pack& pk, const bf16* kg, int lane) {
 }
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
 // Value strip (16 tokens x 16 columns) of one chunk as rows: lane L holds
 // columns 4 (L % 4) .. + 3 of token L / 4, one 8-byte load (zero past the
 // sequence end).
@@ -410,12 +432,25 @@ struct Tiles {
   bf16 o[256];  // O, column-major [column][token]
 };
 
+// Per chunk slot: producer-half syncs (counted over the run; both waves of
+// a slot make the same sequence of them), per state wave the rounds it is
+// done with (a state wave may run rounds ahead of another, so a shared count
+// would not say that all of them left a buffer), and per package buffer and
+// producer wave the last round whose package part that wave finished.
+struct Sync {
+  int half[kPW];
+  int done[kPW][4];
+  int rdy[2][kPW][kPH];
+};
+constexpr int kSyncZeroInts = kPW + kPW * 4;  // then rdy, set to -1
+
 template <int NSW, int SPW>
 struct Smem {
-  Pack pk[2][kPW];          // first: keeps the packages' alignment
-  bf16 kg[kPW][128 * kTok];  // K_G of the round being produced, swizzled rows
-  float tots[kPW][kPH][256]; // per producer wave: 4-token gate totals [group][channel]
+  Pack pk[2][kPW];              // first: keeps the packages' alignment
+  bf16 kg[2][kPW][128 * kTok];  // K_G, with the package buffers, swizzled rows
+  float tots[kPW][kPH][256];    // per producer wave: 4-token gate totals [group][channel]
   Tiles t[NSW][SPW];
+  Sync sy;
 };
 
 template <int VS>
@@ -440,6 +475,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   const int H = p.H;
   // sequence of rank rest / H (longest first, ties by index): from the plan
   // table, or ranked here when there are few sequences
+  if (tid < int(sizeof(Sync) / sizeof(int))) reinterpret_cast<int*>(&sm.sy)[tid] = tid < kSyncZeroInts ? 0 : -1;
   int n;
   if (p.order) {
     n = p.order[rest / H];
@@ -465,7 +501,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
     // resource derived from it stays in scalar registers
     n = __builtin_amdgcn_readfirstlane(seq_sh[0]);
   }
-
+  __syncthreads();  // counters zeroed, ranking scratch read: the packages are free
 
   const int bos = min(max(p.cu[n], 0), p.T);
   const int eos = min(max(p.cu[n + 1], bos), p.T);
@@ -493,27 +529,27 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
     const RawLoad ld{src, p.ts_q, p.ts_k, p.ts_g, p.ts_b, lane, hf};
     Raw raw;
     ld.all(raw, bos + kTok * c);
-    bf16* kg = sm.kg[c];
     float* tots = sm.tots[c][hf];
-    // two barriers per round: operands of both halves, then the products
-    for (int r = 0; r <= nr; ++r) {
+    for (int r = 0; r < nr; ++r) {
       const int j = kPW * r + c;
-      const bool act = r < nr && j < nc;
+      if (j >= nc) break;
       Pack& P = pk[r & 1][c];
-      if (act) {
-        const int t0 = bos + kTok * j, Lc = min(kTok, eos - t0);
-        // this wave's next chunk (one round ahead) is loaded while the
-        // operands are formed
-        const int tn = t0 + kTok * kPW;
-        if (Lc == kTok) produce_operands<true>(P, kg, tots, raw, ld, tn, hf, Lc, lane, c2, c1, lb2, p.scale);
-        else produce_operands<false>(P, kg, tots, raw, ld, tn, hf, Lc, lane, c2, c1, lb2, p.scale);
-      }
-      __syncthreads();
-      if (act) {
-        if (hf == 0) produce_inverse(P, kg, lane);
-        else produce_m(P, kg, lane);
-      }
-      __syncthreads();
+      bf16* kg = sm.kg[r & 1][c];
+      // the buffers are free once every state wave is done with round r - 2
+      if (r >= 2)
+        for (int s = 0; s < NSW; ++s) wait_count(&sm.sy.done[c][s], r - 1);
+      const int t0 = bos + kTok * j, Lc = min(kTok, eos - t0);
+      // this wave's next chunk (one round ahead) is loaded while the operands
+      // are formed
+      const int tn = t0 + kTok * kPW;
+      if (Lc == kTok) produce_operands<true>(P, kg, tots, raw, ld, tn, hf, Lc, lane, c2, c1, lb2, p.scale);
+      else produce_operands<false>(P, kg, tots, raw, ld, tn, hf, Lc, lane, c2, c1, lb2, p.scale);
+      // both halves' operands (the products run over all 128 channels)
+      arrive(&sm.sy.half[c], lane);
+      wait_count(&sm.sy.half[c], kPH * (r + 1));
+      if (hf == 0) produce_inverse(P, kg, lane);
+      else produce_m(P, kg, lane);
+      if (lane == 0) __hip_atomic_store(&sm.sy.rdy[r & 1][c][hf], r, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     return;
   }
@@ -579,18 +615,17 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
       for (int u = 0; u < SPW; ++u) v[c][u] = load_vrow(vsrc, cstrip + 16 * NSW * u, p.ts_v, t0, lane);
     }
   };
-  // chunks of round r - 1, in order, from package buffer B = (r - 1) % 2:
-  // the first kEarly while the producers form their operands, the rest while
-  // they form the products (compile-time indices, so every LDS read is a
-  // lane offset plus a constant)
-  auto consume_half = [&](const uint2 (&v)[kPW][SPW], int r, auto buf, auto half) {
+  // chunks of round r, in order, from package buffer B = r % 2, each once
+  // its producers are done with it (compile-time indices, so every LDS read
+  // is a lane offset plus a constant)
+  auto consume_round = [&](const uint2 (&v)[kPW][SPW], int r, auto buf) {
     constexpr int B = decltype(buf)::value;
-    constexpr int HB = decltype(half)::value;
-    constexpr int C0 = HB ? kEarly : 0, C1 = HB ? kPW : kEarly;
 #pragma unroll
-    for (int c = C0; c < C1; ++c) {
-      const int j = kPW * (r - 1) + c;
+    for (int c = 0; c < kPW; ++c) {
+      const int j = kPW * r + c;
       if (j >= nc) break;
+      wait_count(&sm.sy.rdy[B][c][0], r);
+      wait_count(&sm.sy.rdy[B][c][1], r);
       const Pack& P = pk[B][c];
       const int t0 = bos + kTok * j;
 
@@ -656,26 +691,17 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
           S[u][rt] = mfma16h(a, Nq, S[u][rt] * gm);
         }
       }
+      arrive(&sm.sy.done[c][sw], lane);
     }
   };
 
-  // the producers' two barriers per round: half of the previous round's
-  // chunks before each
   load_round(va, 0);
-  __syncthreads();
-  __syncthreads();
-  for (int r = 1; r <= nr; r += 2) {  // r odd: buffer 0; r + 1: buffer 1
-    load_round(vbuf, r);
-    consume_half(va, r, BufIdx<0>{}, BufIdx<0>{});
-    __syncthreads();
-    consume_half(va, r, BufIdx<0>{}, BufIdx<1>{});
-    __syncthreads();
-    if (r + 1 <= nr) {
-      load_round(va, r + 1);
-      consume_half(vbuf, r + 1, BufIdx<1>{}, BufIdx<0>{});
-      __syncthreads();
-      consume_half(vbuf, r + 1, BufIdx<1>{}, BufIdx<1>{});
-      __syncthreads();
+  for (int r = 0; r < nr; r += 2) {  // r even: buffer 0; r + 1: buffer 1
+    load_round(vbuf, r + 1);
+    consume_round(va, r, BufIdx<0>{});
+    if (r + 1 < nr) {
+      load_round(va, r + 2);
+      consume_round(vbuf, r + 1, BufIdx<1>{});
     }
   }
 
@@ -698,7 +724,6 @@ hipError_t launch_pipe(const Params& p, hipStream_t stream) {
   const void* fn = nullptr;
   int threads = 0;
   switch (kD / p.vsplit) {
-    case 128: fn = reinterpret_cast<const void*>(&pipe_kernel<128>); threads = Cfg<128>::kThreads; break;
     case 64: fn = reinterpret_cast<const void*>(&pipe_kernel<64>); threads = Cfg<64>::kThreads; break;
     case 32: fn = reinterpret_cast<const void*>(&pipe_kernel<32>); threads = Cfg<32>::kThreads; break;
     case 16: fn = reinterpret_cast<const void*>(&pipe_kernel<16>); threads = Cfg<16>::kThreads; break;
