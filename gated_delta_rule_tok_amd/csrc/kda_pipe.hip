@@ -24,9 +24,10 @@
 // slice each) walk the chunks in order, keeping their strip of S (128 x 16
 // fp32) in registers, and apply the three state contractions and the output.
 // There is no workgroup barrier in the main loops: each chunk slot has two
-// package buffers (alternate rounds of four chunks) and LDS flags -- producer
-// halves that formed their operands, the round each producer half last
-// finished per buffer, the rounds each state wave is done with -- so every
+// package buffers (alternate rounds of four chunks) and LDS counters --
+// producer halves that formed their operands, producer halves that finished
+// their package part per buffer, the rounds each state wave is done with
+// (read as one 16-byte row) -- so every
 // wave waits only for the package or buffer it needs next, and the serial
 // state chain, the inverse's latency chain and the next round's operand work
 // overlap on each SIMD (each runs the two VALU-heavy producer waves of one
@@ -200,9 +201,15 @@ struct RawLoad {
       r.k[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.k, col_off(t0, rr, ts_k), 0, 0));
     }
   }
+  // in the loop's issue order (rows, gate, q/k), which the scheduler must
+  // keep: the waits at the top of the loop are computed over both ways in,
+  // so rows issued last here would make the first wait of every round drain
+  // the whole queue
   __device__ __forceinline__ void all(Raw& r, int t0) const {
     rows(r, t0);
+    __builtin_amdgcn_sched_barrier(0);
     gate(r, t0);
+    __builtin_amdgcn_sched_barrier(0);
     qk(r, t0);
   }
 };
@@ -275,6 +282,11 @@ __device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, float* tots
       pk.beta[lane] = lane < Lc ? rcp(1.f + ex2(-kLog2e * bf16_to_f32(uint16_t(raw.beta)))) : 0.f;
     }
   }
+  // the next chunk's rows (tn), into the registers just consumed: they are
+  // the first thing the next round needs, so they get the longest lead
+  __builtin_amdgcn_sched_barrier(0);
+  ld.rows(raw, tn);
+  __builtin_amdgcn_sched_barrier(0);
 
   // gate sigma per (token, channel), its running sum over this lane's 4
   // tokens, then the sum over the earlier token groups (lanes 16 apart, via
@@ -341,7 +353,6 @@ __device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, float* tots
   }
   __builtin_amdgcn_sched_barrier(0);
   ld.qk(raw, tn);
-  ld.rows(raw, tn);
 }
 
 // Producer, second phase, first wave of a chunk: A = X K_G^T and A^T over the
@@ -432,17 +443,38 @@ struct Tiles {
   bf16 o[256];  // O, column-major [column][token]
 };
 
-// Per chunk slot: producer-half syncs (counted over the run; both waves of
-// a slot make the same sequence of them), per state wave the rounds it is
-// done with (a state wave may run rounds ahead of another, so a shared count
-// would not say that all of them left a buffer), and per package buffer and
-// producer wave the last round whose package part that wave finished.
+// Per chunk slot: per state wave the rounds it is done with (a state wave
+// may run rounds ahead of another, so a shared count would not say that all
+// of them left a buffer; one 16-byte row, read at once), producer-half syncs
+// (counted over the run; both waves of a slot make the same sequence of
+// them), and per package buffer the producer halves' finished package parts
+// (both halves add one per round on that buffer).  All start at zero.
 struct Sync {
-  int half[kPW];
   int done[kPW][4];
-  int rdy[2][kPW][kPH];
+  int half[kPW];
+  int rdy[2][kPW];
 };
-constexpr int kSyncZeroInts = kPW + kPW * 4;  // then rdy, set to -1
+
+// Wait until the first n counters of a 16-byte row are all >= target: one
+// LDS read per poll (same bound and argument as wait_count).  Used before
+// overwriting what the counting waves have read: their release made those
+// reads complete, the caller's writes are issued only after the exit branch
+// (which waits for the value), and the compiler barrier keeps them there.
+template <int n>
+__device__ __forceinline__ void wait_row(const int* row, int target) {
+#pragma unroll 1
+  for (int it = 0; it < kSpinMax; ++it) {
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) const volatile i32x4 lds_row;
+    const i32x4 d = *(lds_row*)(row);
+    int m = d[0];
+    if (n > 1) m = min(m, d[1]);
+    if (n > 2) m = min(m, min(d[2], d[3]));
+    if (__builtin_amdgcn_readfirstlane(m) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 template <int NSW, int SPW>
 struct Smem {
@@ -475,7 +507,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   const int H = p.H;
   // sequence of rank rest / H (longest first, ties by index): from the plan
   // table, or ranked here when there are few sequences
-  if (tid < int(sizeof(Sync) / sizeof(int))) reinterpret_cast<int*>(&sm.sy)[tid] = tid < kSyncZeroInts ? 0 : -1;
+  if (tid < int(sizeof(Sync) / sizeof(int))) reinterpret_cast<int*>(&sm.sy)[tid] = 0;
   int n;
   if (p.order) {
     n = p.order[rest / H];
@@ -537,19 +569,21 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
       bf16* kg = sm.kg[r & 1][c];
       // the buffers are free once every state wave is done with round r - 2
       if (r >= 2)
-        for (int s = 0; s < NSW; ++s) wait_count(&sm.sy.done[c][s], r - 1);
+        wait_row<NSW>(sm.sy.done[c], r - 1);
       const int t0 = bos + kTok * j, Lc = min(kTok, eos - t0);
       // this wave's next chunk (one round ahead) is loaded while the operands
       // are formed
       const int tn = t0 + kTok * kPW;
-      if (Lc == kTok) produce_operands<true>(P, kg, tots, raw, ld, tn, hf, Lc, lane, c2, c1, lb2, p.scale);
-      else produce_operands<false>(P, kg, tots, raw, ld, tn, hf, Lc, lane, c2, c1, lb2, p.scale);
+      // one code path for full and partial chunks: with two, the registers
+      // of the next chunk's loads differ between them and the merge copies
+      // them, which waits for the loads at the end of every round
+      produce_operands<false>(P, kg, tots, raw, ld, tn, hf, Lc, lane, c2, c1, lb2, p.scale);
       // both halves' operands (the products run over all 128 channels)
       arrive(&sm.sy.half[c], lane);
       wait_count(&sm.sy.half[c], kPH * (r + 1));
       if (hf == 0) produce_inverse(P, kg, lane);
       else produce_m(P, kg, lane);
-      if (lane == 0) __hip_atomic_store(&sm.sy.rdy[r & 1][c][hf], r, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      arrive(&sm.sy.rdy[r & 1][c], lane);
     }
     return;
   }
@@ -624,8 +658,8 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
     for (int c = 0; c < kPW; ++c) {
       const int j = kPW * r + c;
       if (j >= nc) break;
-      wait_count(&sm.sy.rdy[B][c][0], r);
-      wait_count(&sm.sy.rdy[B][c][1], r);
+      // both halves of the package: rounds B, B + 2, .., r on this buffer
+      wait_count(&sm.sy.rdy[B][c], kPH * ((r >> 1) + 1));
       const Pack& P = pk[B][c];
       const int t0 = bos + kTok * j;
 
@@ -644,6 +678,18 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
       const f32x4 rqR = *reinterpret_cast<const f32x4*>(&P.rqs[4 * g4]);
       const bf16x4 Lf = *reinterpret_cast<const bf16x4*>(&P.l[frag(0, l16, 4 * g4)]);
       const bf16x4 Mf = *reinterpret_cast<const bf16x4*>(&P.m[frag(0, l16, 4 * g4)]);
+      // V in the accumulator layout (it does not depend on S, so it is formed
+      // before the chain): the row tile read back transposed (lane l16 of
+      // group g4: column l16 of tokens 4 g4 .. 4 g4 + 3); this wave's own LDS
+      // accesses are processed in order
+      f32x4 V[SPW];
+#pragma unroll
+      for (int u = 0; u < SPW; ++u) {
+        Tiles& tl = sm.t[sw][u];
+        *reinterpret_cast<uint2*>(&tl.v[4 * lane]) = v[c][u];
+        __builtin_amdgcn_wave_barrier();
+        V[u] = to_f32x4(tr4(&tl.v[4 * lane]));
+      }
 
 #pragma unroll
       for (int u = 0; u < SPW; ++u) {
@@ -657,14 +703,20 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
           Y = mfma32(ax[kb2], Sb[kb2], Y);
           Q = mfma32(aq[kb2], Sb[kb2], Q);
         }
-        // V in the accumulator layout: the row tile read back transposed
-        // (lane l16 of group g4: column l16 of tokens 4 g4 .. 4 g4 + 3); this
-        // wave's own LDS accesses are processed in order
+        // the products are issued here; the decay Diag(e^{G_last}) of the
+        // state (its bf16 copy is already taken) is applied while they run,
+        // before their results are used (a wave issues in order, so anything
+        // placed after that point would lengthen the chain to the update)
+        asm volatile("" : "+v"(Y), "+v"(Q));
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
+          const f32x4 gm = *reinterpret_cast<const f32x4*>(&P.gam[16 * rt + 4 * g4]);
+          S[u][rt] = S[u][rt] * gm;
+        }
+        asm volatile("" : "+v"(S[u][0]), "+v"(S[u][1]), "+v"(S[u][2]), "+v"(S[u][3]),
+                     "+v"(S[u][4]), "+v"(S[u][5]), "+v"(S[u][6]), "+v"(S[u][7]), "+v"(Y), "+v"(Q));
         Tiles& tl = sm.t[sw][u];
-        *reinterpret_cast<uint2*>(&tl.v[4 * lane]) = v[c][u];
-        __builtin_amdgcn_wave_barrier();
-        const f32x4 V = to_f32x4(tr4(&tl.v[4 * lane]));
-        const f32x4 D = V - Y;
+        const f32x4 D = V[u] - Y;
         const f32x4 N = mfma16(Lf, to_bf16x4(D), bR * D);
         const f32x4 O = mfma16(Mf, to_bf16x4(N), rqR * Q);
         // O into rows: written column-major, read back transposed (lane l16
@@ -677,18 +729,17 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
             __builtin_bit_cast(u32x2, orow), odst,
             ((unsigned(t0) + unsigned(l16)) * unsigned(p.ts_o) + cstrip + 16 * NSW * u + 4u * g4) * 2u,
             0, 0);
-        // S <- Diag(e^{G_last}) S + K'^T N in fp16 operands (kKpScale K' and
+        // S <- (Diag(e^{G_last}) S) + K'^T N in fp16 operands (kKpScale K' and
         // kNScale N; k-slots: this lane group's four tokens).  The accumulator
-        // comes from the VALU (S gm), never straight from a product of another
-        // MFMA shape: on gfx950 a 16x16x16 product accumulating onto a
-        // 16x16x32 result was observed to return wrong sums.
+        // comes from the VALU (the decay above), never straight from a product
+        // of another MFMA shape: on gfx950 a 16x16x16 product accumulating onto
+        // a 16x16x32 result was observed to return wrong sums.
         const f16x4 Nq = f16x4{(_Float16)(N[0] * kNScale), (_Float16)(N[1] * kNScale),
                                (_Float16)(N[2] * kNScale), (_Float16)(N[3] * kNScale)};
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
-          const f32x4 gm = *reinterpret_cast<const f32x4*>(&P.gam[16 * rt + 4 * g4]);
           const f16x4 a = *reinterpret_cast<const f16x4*>(&P.kp[frag(rt, l16, 4 * g4)]);
-          S[u][rt] = mfma16h(a, Nq, S[u][rt] * gm);
+          S[u][rt] = mfma16h(a, Nq, S[u][rt]);
         }
       }
       arrive(&sm.sy.done[c][sw], lane);
