@@ -91,6 +91,15 @@ __device__ __forceinline__ int swz(int r) { return r ^ ((r >> 2) & 3); }
 __device__ __forceinline__ int frag(int blk, int m, int k) {
   return blk * 256 + ((k >> 2) * 16 + m) * 4 + (k & 3);
 }
+// The same with the row m of each 8-byte unit permuted by its k group
+// (m ^ (k / 4) in the two low bits).  For K' the producers write one key's
+// four tokens per lane, and the lanes of a store differ in key only by
+// multiples of 4 within their token group: in plain fragment order that puts
+// 16 lanes on one bank pair; permuted, the 64 lanes spread over 16.  The
+// reader's 512 contiguous bytes per block only change order.
+__device__ __forceinline__ int fragx(int blk, int m, int k) {
+  return frag(blk, m ^ ((k >> 2) & 3), k);
+}
 
 // Buffer resources over one head's rows of a [T, H, ...] tensor, bounded at
 // the end of the sequence: loads past it return 0 and stores past it are
@@ -132,7 +141,7 @@ __device__ __forceinline__ void wait_count(const int* ctr, int target) {
 struct Pack {
   bf16 x[128 * kTok];    // X = e^{G} k~, swizzled rows
   bf16 qt[128 * kTok];   // Q_T = e^{G} q, swizzled rows
-  bf16 kp[128 * kTok];   // kKpScale K' as fp16, fragment order (block = 16 keys)
+  bf16 kp[128 * kTok];   // kKpScale K' as fp16, permuted fragment order (fragx; block = 16 keys)
   bf16 l[256];           // L, fragment order
   bf16 m[256];           // M', fragment order
   float beta[kTok];
@@ -348,7 +357,7 @@ __device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, float* tots
     *reinterpret_cast<uint2*>(&pk.x[row]) = uint2{pk2(vx[0], vx[1]), pk2(vx[2], vx[3])};
     *reinterpret_cast<uint2*>(&pk.qt[row]) = uint2{pk2(vq[0], vq[1]), pk2(vq[2], vq[3])};
     *reinterpret_cast<uint2*>(&kg[row]) = uint2{pk2(vg[0], vg[1]), pk2(vg[2], vg[3])};
-    *reinterpret_cast<uint2*>(&pk.kp[frag(c >> 4, c & 15, 4 * tq)]) =
+    *reinterpret_cast<uint2*>(&pk.kp[fragx(c >> 4, c & 15, 4 * tq)]) =
         uint2{pk2h(vk[0], vk[1]), pk2h(vk[2], vk[3])};
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -738,7 +747,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
                                (_Float16)(N[2] * kNScale), (_Float16)(N[3] * kNScale)};
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
-          const f16x4 a = *reinterpret_cast<const f16x4*>(&P.kp[frag(rt, l16, 4 * g4)]);
+          const f16x4 a = *reinterpret_cast<const f16x4*>(&P.kp[fragx(rt, l16, 4 * g4)]);
           S[u][rt] = mfma16h(a, Nq, S[u][rt]);
         }
       }
