@@ -242,6 +242,13 @@ __device__ __forceinline__ float quad_perm(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
+// Lane N of this lane's row of 16 (DPP row_newbcast; the backend folds it
+// into the consuming VALU instruction).
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xF, 0xF, false));
+}
+
 // Sum over the four lanes of a quad.
 __device__ __forceinline__ float quad_sum(float s) {
   s += quad_perm<0xB1>(s);  // [1,0,3,2]
@@ -275,7 +282,7 @@ __device__ __forceinline__ float chan(uint2 w, int i) {
 // (fp16), gam, and rqs (second half) or beta (first half).  FULL: all 16
 // tokens are inside the sequence (no masking).
 template <bool FULL>
-__device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, float* tots, Raw& raw,
+__device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, Raw& raw,
                                                  const RawLoad& ld, int tn, int hf, int Lc, int lane,
                                                  const float* c2, float c1, float lb2, float scale) {
   const int cg = lane & 15, tq = lane >> 4;
@@ -298,8 +305,9 @@ __device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, float* tots
   __builtin_amdgcn_sched_barrier(0);
 
   // gate sigma per (token, channel), its running sum over this lane's 4
-  // tokens, then the sum over the earlier token groups (lanes 16 apart, via
-  // LDS); the log2 decay of a token is lb2 * sigma (lb2 = lower_bound log2 e)
+  // tokens, then the sum over the earlier token groups (lanes 16 apart, by
+  // lane permutes); the log2 decay of a token is lb2 * sigma (lb2 =
+  // lower_bound log2 e)
   float cs[4][4];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
@@ -314,21 +322,21 @@ __device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, float* tots
   __builtin_amdgcn_sched_barrier(0);
   ld.gate(raw, tn);  // the next chunk's (tn), into the registers just consumed
   __builtin_amdgcn_sched_barrier(0);
-  // tots[g][4 cg + i]: the 4-token total of group g for channel 4 cg + i
-  *reinterpret_cast<f32x4*>(&tots[64 * tq + 4 * cg]) = f32x4{cs[0][3], cs[1][3], cs[2][3], cs[3][3]};
-  __builtin_amdgcn_wave_barrier();
-  f32x4 excl = {0.f, 0.f, 0.f, 0.f}, all = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const f32x4 t = *reinterpret_cast<const f32x4*>(&tots[64 * g + 4 * cg]);
-    all += t;
-    if (g < tq) excl += t;
-  }
+  // the 4-token totals of the other token groups of this channel (rows of 16
+  // lanes): permlane16_swap gives each lane its row pair's even and odd row,
+  // permlane32_swap the two pairs' sums; no LDS round trip
   float off[4], gam[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    off[i] = lb2 * excl[i];
-    gam[i] = ex2(lb2 * all[i]);  // e^{G_last}
+    const unsigned t = __float_as_uint(cs[i][3]);
+    const auto pr = __builtin_amdgcn_permlane16_swap(t, t, false, false);
+    const float te = __uint_as_float(pr[0]), to = __uint_as_float(pr[1]);  // rows tq & ~1, tq | 1
+    const unsigned pp = __float_as_uint(te + to);
+    const auto pq = __builtin_amdgcn_permlane32_swap(pp, pp, false, false);
+    const float p01 = __uint_as_float(pq[0]), p23 = __uint_as_float(pq[1]);  // rows 0 + 1, 2 + 3
+    const float excl = ((tq & 2) ? p01 : 0.f) + ((tq & 1) ? te : 0.f);      // groups before tq
+    off[i] = lb2 * excl;
+    gam[i] = ex2(lb2 * (p01 + p23));  // e^{G_last}
   }
   if (tq == 0)
     *reinterpret_cast<f32x4*>(&pk.gam[64 * hf + 4 * cg]) = f32x4{gam[0], gam[1], gam[2], gam[3]};
@@ -434,6 +442,21 @@ __device__ __forceinline__ void produce_m(Pack& pk, const bf16* kg, int lane) {
 }
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// S <- Diag(e^{G_last}) S on one state strip in the accumulator layout (lane
+// (l16, g4) holds rows 16 rt + 4 g4 + j).  Each lane has read two of its
+// row's 32 factors, g[16 (l16 / 2) + 4 g4 + 2 (l16 % 2) + {0, 1}], so row rt,
+// element j sits in lane 2 rt + j / 2 of the same 16 (component j % 2): one
+// 8-byte LDS read per lane instead of eight 16-byte ones, and the broadcast
+// rides on the multiply.
+template <int RT = 0>
+__device__ __forceinline__ void decay_strip(f32x4 (&S)[8], float g0, float g1) {
+  S[RT][0] = S[RT][0] * row_bcast<2 * RT>(g0);
+  S[RT][1] = S[RT][1] * row_bcast<2 * RT>(g1);
+  S[RT][2] = S[RT][2] * row_bcast<2 * RT + 1>(g0);
+  S[RT][3] = S[RT][3] * row_bcast<2 * RT + 1>(g1);
+  if constexpr (RT < 7) decay_strip<RT + 1>(S, g0, g1);
+}
 // Value strip (16 tokens x 16 columns) of one chunk as rows: lane L holds
 // columns 4 (L % 4) .. + 3 of token L / 4, one 8-byte load (zero past the
 // sequence end).
@@ -489,7 +512,6 @@ template <int NSW, int SPW>
 struct Smem {
   Pack pk[2][kPW];              // first: keeps the packages' alignment
   bf16 kg[2][kPW][128 * kTok];  // K_G, with the package buffers, swizzled rows
-  float tots[kPW][kPH][256];    // per producer wave: 4-token gate totals [group][channel]
   Tiles t[NSW][SPW];
   Sync sy;
 };
@@ -570,7 +592,6 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
     const RawLoad ld{src, p.ts_q, p.ts_k, p.ts_g, p.ts_b, lane, hf};
     Raw raw;
     ld.all(raw, bos + kTok * c);
-    float* tots = sm.tots[c][hf];
     for (int r = 0; r < nr; ++r) {
       const int j = kPW * r + c;
       if (j >= nc) break;
@@ -586,7 +607,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
       // one code path for full and partial chunks: with two, the registers
       // of the next chunk's loads differ between them and the merge copies
       // them, which waits for the loads at the end of every round
-      produce_operands<false>(P, kg, tots, raw, ld, tn, hf, Lc, lane, c2, c1, lb2, p.scale);
+      produce_operands<false>(P, kg, raw, ld, tn, hf, Lc, lane, c2, c1, lb2, p.scale);
       // both halves' operands (the products run over all 128 channels)
       arrive(&sm.sy.half[c], lane);
       wait_count(&sm.sy.half[c], kPH * (r + 1));
@@ -717,10 +738,9 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
         // before their results are used (a wave issues in order, so anything
         // placed after that point would lengthen the chain to the update)
         asm volatile("" : "+v"(Y), "+v"(Q));
-#pragma unroll
-        for (int rt = 0; rt < 8; ++rt) {
-          const f32x4 gm = *reinterpret_cast<const f32x4*>(&P.gam[16 * rt + 4 * g4]);
-          S[u][rt] = S[u][rt] * gm;
+        {
+          const float2 gv = *reinterpret_cast<const float2*>(&P.gam[16 * (l16 >> 1) + 4 * g4 + 2 * (l16 & 1)]);
+          decay_strip(S[u], gv.x, gv.y);
         }
         asm volatile("" : "+v"(S[u][0]), "+v"(S[u][1]), "+v"(S[u][2]), "+v"(S[u][3]),
                      "+v"(S[u][4]), "+v"(S[u][5]), "+v"(S[u][6]), "+v"(S[u][7]), "+v"(Y), "+v"(Q));
