@@ -108,6 +108,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--sets", type=int, default=2, help="buffer sets rotated across steps")
+    ap.add_argument("--checkpoint-interval", type=int, default=0,
+                    help="also write the state every this many tokens of each sequence "
+                         "(kda_chunk_prefill_fwd_checkpoints); 0: off")
     ap.add_argument("--settle-ms", type=float, default=200.0,
                     help="run the call this long before the warmup steps (clock ramp; 0: none)")
     ap.add_argument("--traffic-from", metavar="PMC_DIR",
@@ -179,13 +182,18 @@ def main():
         s["fin"] = torch.empty(N, H, 128, 128, dtype=sdtype, device=dev)
         s["ws"] = torch.empty(max(1, kda.kda_get_workspace_size(T, H, N)), dtype=torch.uint8,
                               device=dev)
+        s["ck"] = (torch.empty(T // args.checkpoint_interval, H, 128, 128, dtype=sdtype, device=dev)
+                   if args.checkpoint_interval else None)
         sets.append(s)
+    lens = np.diff(x.cu_seqlens)
+    n_ck = int((lens // args.checkpoint_interval).sum()) if args.checkpoint_interval else 0
 
     def step(i):
         s = sets[i % len(sets)]
         kda.kda_chunk_prefill_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["A_log"],
                                   s["dt_bias"], x.lower_bound, x.scale, s["s0"], s["cu"],
-                                  s["out"], s["fin"], s["ws"])
+                                  s["out"], s["fin"], s["ws"], checkpoints=s["ck"],
+                                  checkpoint_interval=args.checkpoint_interval)
 
     # The device's clocks ramp up over the first ~20 ms of this load (one
     # launch went from about 184 to 148 us over its first ~120 calls), so the
@@ -232,7 +240,9 @@ def main():
             with torch.cuda.graph(graph, stream=cap):
                 kda.kda_chunk_prefill_fwd(s0["q"], s0["k"], s0["v"], s0["g"], s0["beta"],
                                           s0["A_log"], s0["dt_bias"], x.lower_bound, x.scale,
-                                          s0["s0"], s0["cu"], s0["out"], s0["fin"], s0["ws"])
+                                          s0["s0"], s0["cu"], s0["out"], s0["fin"], s0["ws"],
+                                          checkpoints=s0["ck"],
+                                          checkpoint_interval=args.checkpoint_interval)
         torch.cuda.synchronize()
         # the capture left the device idle: settle the clocks again (~100 ms)
         c0 = time.perf_counter()
@@ -265,11 +275,12 @@ def main():
     del cbuf, cdst
     tokens_per_s = T / (ms_per_step * 1e-3)
     abytes = algorithmic_bytes(T, H, N, sbytes, x.initial_state is not None)
+    abytes += n_ck * H * 128 * 128 * sbytes  # checkpoint states written
     achieved_gbs = abytes / (launch_ms * 1e-3) / 1e9
 
     traffic = None
     tf = traffic_file(x.meta["config"])
-    if os.path.exists(tf):
+    if os.path.exists(tf) and not args.checkpoint_interval:  # counters of the plain call
         t = json.load(open(tf))
         if t.get("kernel_source_sha256") == kernel_source_hash():
             traffic = t["bytes_per_launch"]
@@ -295,7 +306,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": x.meta["config"], "tokens": T, "sequences": N, "heads": H,
                    "head_dim": 128, "state": "bf16" if x.state_bf16 else "fp32",
-                   "initial_state": x.initial_state is not None, "buffer_sets": len(sets)},
+                   "initial_state": x.initial_state is not None, "buffer_sets": len(sets),
+                   **({"checkpoint_interval": args.checkpoint_interval, "checkpoints": n_ck}
+                      if args.checkpoint_interval else {})},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": abytes, "launch_us": launch_ms * 1e3,

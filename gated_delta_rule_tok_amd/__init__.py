@@ -81,6 +81,10 @@ def load_library():
                                                       P, I64, I32, I32, ctypes.c_int, SZ,
                                                       ctypes.POINTER(_Strides)]
         lib.kda_chunk_prefill_fwd_strided.restype = ctypes.c_int
+        lib.kda_chunk_prefill_fwd_checkpoints.argtypes = [
+            P, P, P, P, P, P, P, F, F, P, P, P, P, P, P, I64, I32, I32, ctypes.c_int, SZ,
+            ctypes.POINTER(_Strides), P, I32, I64]
+        lib.kda_chunk_prefill_fwd_checkpoints.restype = ctypes.c_int
         lib.kda_status_string.argtypes = [ctypes.c_int]
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_last_hip_error.argtypes = []
@@ -146,7 +150,7 @@ def _check(t, name, dtype, shape=None, strided=False):
 
 def kda_chunk_prefill_fwd(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound: float,
                           scale: float, initial_state, cu_seqlens, out, final_state, workspace,
-                          stream=None) -> None:
+                          stream=None, checkpoints=None, checkpoint_interval: int = 0) -> None:
     """Queue one KDA chunked-prefill forward (see include/kda.h for the contract).
 
     q, k, v, g, out [T, H, 128] bf16; beta_logits [T, H] bf16; A_log [H] fp32;
@@ -155,7 +159,9 @@ def kda_chunk_prefill_fwd(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound: 
     cu_seqlens [N + 1] int32; workspace uint8 (or None if no workspace is
     needed); stream: a torch.cuda.Stream, a raw hipStream_t int, or None for
     torch's current stream.  Leading singleton batch dims ([1, T, H, 128]) are
-    accepted.
+    accepted.  checkpoints: None, or [C, H, 128, 128] in the state dtype to
+    receive the state after every checkpoint_interval tokens of each sequence
+    (kda_chunk_prefill_fwd_checkpoints; C >= T // checkpoint_interval).
     """
     import torch
     lib = load_library()
@@ -209,14 +215,24 @@ def kda_chunk_prefill_fwd(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound: 
         stream = stream.cuda_stream
     args = (*ptrs, float(lower_bound), float(scale), s0, cu, o, fs, ws,
             ctypes.c_void_p(int(stream)), T, H, N, sdt, wsb)
-    if all(t.is_contiguous() for t in views.values()):
-        rc = lib.kda_chunk_prefill_fwd(*args)
-    else:
+    st = None
+    if not all(t.is_contiguous() for t in views.values()):
         st = _Strides()
         for name in ("q", "k", "v", "g", "out"):
             setattr(st, f"{name}_token", views[name].stride(0))
             setattr(st, f"{name}_head", views[name].stride(1))
         st.beta_token, st.beta_head = views["beta"].stride(0), views["beta"].stride(1)
+    if checkpoints is not None:
+        if checkpoints.dim() != 4:
+            raise ValueError("checkpoints must be [C, H, 128, 128]")
+        ck = _check(checkpoints, "checkpoints", final_state.dtype,
+                    (checkpoints.shape[0], H, HEAD_DIM, HEAD_DIM))
+        rc = lib.kda_chunk_prefill_fwd_checkpoints(
+            *args, None if st is None else ctypes.byref(st), ck, int(checkpoint_interval),
+            int(checkpoints.shape[0]))
+    elif st is None:
+        rc = lib.kda_chunk_prefill_fwd(*args)
+    else:
         rc = lib.kda_chunk_prefill_fwd_strided(*args, ctypes.byref(st))
     if rc != KDA_OK:
         detail = lib.kda_last_hip_error().decode() if rc == 4 else ""

@@ -121,7 +121,8 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
                      const int32_t* cu_seqlens, void* out, void* final_state, void* workspace,
                      void* stream, int64_t num_tokens, int32_t heads, int32_t num_seqs,
                      kda_state_dtype_t state_dtype, size_t workspace_bytes,
-                     const kda_strides_t& sd) {
+                     const kda_strides_t& sd, void* checkpoints = nullptr, int32_t ck_interval = 0,
+                     int64_t ck_capacity = 0) {
   // ---- checks (no HIP call before they pass) --------------------------------
   if (num_tokens < 0 || num_tokens > INT32_MAX) return KDA_ERR_INVALID_ARG;  // int32 offsets
   // per-token tensors may be empty (and NULL) only when there are no tokens
@@ -147,6 +148,11 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   if (state_dtype != KDA_STATE_FP32 && state_dtype != KDA_STATE_BF16) return KDA_ERR_INVALID_ARG;
   if (!std::isfinite(lower_bound) || !std::isfinite(scale)) return KDA_ERR_INVALID_ARG;
   if (lower_bound > 0.f || lower_bound < KDA_LOWER_BOUND_MIN) return KDA_ERR_UNSUPPORTED;
+  if (checkpoints) {
+    if (ck_interval <= 0 || ck_interval % 16) return KDA_ERR_INVALID_ARG;
+    if (ck_capacity < num_tokens / ck_interval) return KDA_ERR_INVALID_ARG;
+    if (lower_bound < kda::kPipeLowerBoundMin) return KDA_ERR_UNSUPPORTED;
+  }
   const size_t need = kda_get_workspace_size(num_tokens, heads, num_seqs);
   if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
   if (need > 0 && !workspace) return KDA_ERR_INVALID_ARG;
@@ -183,6 +189,9 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   p.N = num_seqs;
   p.vsplit = s;
   p.state_bf16 = state_dtype == KDA_STATE_BF16;
+  p.ck = checkpoints;
+  p.ck_int = ck_interval;
+  p.ck_cap = ck_capacity;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   // the pipelined kernel takes lower_bound >= -5 and slices of <= 64 value
@@ -193,9 +202,12 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   // average): the decode kernel streams each state once with 16-byte
   // accesses; the chunked kernels' machinery does not pay off there
   if (override == 0 && num_tokens <= kda::kDecodeTokensPerSeq * int64_t(num_seqs)) kernel = 3;
+  // checkpoints: the pipelined kernel only, whatever the call's size
+  if (checkpoints && override == 0) kernel = 0;
   if (kernel == 0 && lower_bound < kda::kPipeLowerBoundMin) kernel = 1;
   if (kernel == 0 && p.vsplit == 1) p.vsplit = forced > 0 ? 1 : 2;
   if (kernel == 0 && p.vsplit == 1) kernel = 1;
+  if (checkpoints && kernel != 0) return KDA_ERR_UNSUPPORTED;
   // the sequence order table (longest first): the pipelined kernel ranks a
   // few sequences itself, the decode path takes them in index order, the
   // others read the table
@@ -234,6 +246,23 @@ kda_status_t kda_chunk_prefill_fwd(const void* q, const void* k, const void* v, 
   return forward(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, scale, initial_state,
                  cu_seqlens, out, final_state, workspace, stream, num_tokens, heads, num_seqs,
                  state_dtype, workspace_bytes, dense);
+}
+
+kda_status_t kda_chunk_prefill_fwd_checkpoints(
+    const void* q, const void* k, const void* v, const void* g, const void* beta_logits,
+    const float* A_log, const float* dt_bias, float lower_bound, float scale,
+    const void* initial_state, const int32_t* cu_seqlens, void* out, void* final_state,
+    void* workspace, void* stream, int64_t num_tokens, int32_t heads, int32_t num_seqs,
+    kda_state_dtype_t state_dtype, size_t workspace_bytes, const kda_strides_t* strides,
+    void* checkpoints, int32_t checkpoint_interval, int64_t checkpoint_capacity) {
+  if (!checkpoints) return KDA_ERR_INVALID_ARG;
+  const int64_t row = int64_t(heads) * KDA_HEAD_DIM;
+  const kda_strides_t dense{row, KDA_HEAD_DIM, row, KDA_HEAD_DIM, row,   KDA_HEAD_DIM,
+                            row, KDA_HEAD_DIM, heads, 1,          row, KDA_HEAD_DIM};
+  return forward(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, scale, initial_state,
+                 cu_seqlens, out, final_state, workspace, stream, num_tokens, heads, num_seqs,
+                 state_dtype, workspace_bytes, strides ? *strides : dense, checkpoints,
+                 checkpoint_interval, checkpoint_capacity);
 }
 
 kda_status_t kda_chunk_prefill_fwd_strided(

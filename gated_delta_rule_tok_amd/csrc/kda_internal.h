@@ -39,6 +39,11 @@ struct Params {
   int N;
   int vsplit;      // value-dimension slices per (sequence, head)
   int state_bf16;  // 0: fp32 state, 1: bf16 state
+  // checkpoint states (pipelined kernel only): null, or [ck_cap, H, D, D] in
+  // the state dtype, one after every ck_int tokens of each sequence
+  void* ck;
+  int ck_int;
+  int64_t ck_cap;
 };
 
 // ---- bf16 helpers (bf16 is the high half of an IEEE fp32) -------------------

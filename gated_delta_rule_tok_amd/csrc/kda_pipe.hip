@@ -629,6 +629,46 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   const __amdgpu_buffer_rsrc_t odst = rows_rsrc(p.out + size_t(h) * p.hs_o, eos, p.ts_o, kD);
   const size_t sbase = (size_t(n) * H + h) * kD * kD;
   f32x4 S[SPW][8];
+  // this wave's strips of the state, in the state dtype, into the [D, D]
+  // block at dst + base
+  auto store_state = [&](void* dst, size_t base) {
+    if (p.state_bf16) {
+#pragma unroll
+      for (int u = 0; u < SPW; ++u)
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            static_cast<bf16*>(dst)[base + size_t(16 * rt + 4 * g4 + j) * kD + colb + 16 * NSW * u] =
+                (bf16)S[u][rt][j];
+    } else {
+#pragma unroll
+      for (int u = 0; u < SPW; ++u)
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            static_cast<float*>(dst)[base + size_t(16 * rt + 4 * g4 + j) * kD + colb + 16 * NSW * u] =
+                S[u][rt][j];
+    }
+  };
+  // checkpoint states: the first slot of this sequence (the checkpoints of
+  // the sequences before it, summed over the lanes), the chunk count of the
+  // next checkpoint and its slot
+  int ck_slot = 0, ck_next = 0, ck_chunks = 0;
+  if (p.ck) {
+    int acc = 0;
+    for (int m = lane; m < n; m += 64) {
+      const int b0 = min(max(p.cu[m], 0), p.T);
+      const int e0 = min(max(p.cu[m + 1], b0), p.T);
+      acc += (e0 - b0) / p.ck_int;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    ck_slot = __builtin_amdgcn_readfirstlane(acc);
+    ck_chunks = p.ck_int / kTok;
+    ck_next = ck_chunks;
+  }
   if (!p.s0) {
 #pragma unroll
     for (int u = 0; u < SPW; ++u)
@@ -772,6 +812,14 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
         }
       }
       arrive(&sm.sy.done[c][sw], lane);
+      // the state after the first (j + 1) chunks, when that is a checkpoint
+      // (whole chunks only: a sequence's last, partial chunk never ends on
+      // a multiple of the interval)
+      if (p.ck && j + 1 == ck_next && kTok * (j + 1) <= eos - bos) {
+        if (ck_slot < p.ck_cap) store_state(p.ck, (size_t(ck_slot) * H + h) * kD * kD);
+        ++ck_slot;
+        ck_next += ck_chunks;
+      }
     }
   };
 
@@ -785,17 +833,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
     }
   }
 
-  // final state
-#pragma unroll
-  for (int u = 0; u < SPW; ++u)
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const size_t idx = sbase + size_t(16 * rt + 4 * g4 + j) * kD + colb + 16 * NSW * u;
-        if (p.state_bf16) static_cast<bf16*>(p.sT)[idx] = (bf16)S[u][rt][j];
-        else static_cast<float*>(p.sT)[idx] = S[u][rt][j];
-      }
+  store_state(p.sT, sbase);  // final state
 }
 
 }  // namespace

@@ -153,6 +153,54 @@ kda_status_t kda_chunk_prefill_fwd_strided(
     void* workspace, void* stream, int64_t num_tokens, int32_t heads, int32_t num_seqs,
     kda_state_dtype_t state_dtype, size_t workspace_bytes, const kda_strides_t* strides);
 
+/*
+ * kda_chunk_prefill_fwd (or, with strides, kda_chunk_prefill_fwd_strided) that
+ * also writes checkpoint states: the state of each sequence after every
+ * `checkpoint_interval` of its tokens.  The PR #56485 report ("Features and
+ * motivation") names the kernel's checkpoint state, the intermediate
+ * breakpoint used to link a sequence's state across segments, and stores it
+ * in the state dtype; the pages give no layout, so this one is the plainest:
+ *
+ *   checkpoints          device, state dtype (as final_state), laid out
+ *                        [checkpoint_capacity, heads, 128, 128] (row = key).
+ *                        Sequence n of length L_n writes floor(L_n / interval)
+ *                        states; the j-th (j = 1, 2, ..) is the state after
+ *                        its first j * interval tokens (computed from
+ *                        initial_state like final_state) and goes to slot
+ *                        sum_{m < n} floor(L_m / interval) + j - 1.  A
+ *                        sequence whose length is a multiple of the interval
+ *                        ends with a copy of its final state.  Slots not
+ *                        named this way are not written.
+ *   checkpoint_interval  tokens between checkpoints, a positive multiple of
+ *                        16 (the pipelined kernel's chunk).
+ *   checkpoint_capacity  slots in checkpoints: at least
+ *                        num_tokens / checkpoint_interval (rounded down),
+ *                        which bounds what well-formed cu_seqlens can name;
+ *                        slots past the capacity (malformed cu_seqlens) are
+ *                        never written.
+ *   strides              NULL: the dense layout; else as for
+ *                        kda_chunk_prefill_fwd_strided.
+ *
+ * Every other argument, limit and guarantee is that of the forward call.
+ * The work runs on the pipelined kernel whatever the call's size, so out and
+ * final_state are bit for bit those of the forward call except for
+ * decode-sized calls (at most 8 tokens per sequence on average), where the
+ * forward call takes the token-serial decode kernel (both within the
+ * tolerances of the oracle).  Returns
+ * KDA_ERR_INVALID_ARG for a NULL checkpoints, a bad interval or a short
+ * capacity, and KDA_ERR_UNSUPPORTED for lower_bound < -5 (that range is
+ * served by the 64-token kernel, which writes no checkpoints) or under a
+ * kda_debug_set_kernel / kda_debug_set_vsplit override that selects a kernel
+ * other than the pipelined one.
+ */
+kda_status_t kda_chunk_prefill_fwd_checkpoints(
+    const void* q, const void* k, const void* v, const void* g, const void* beta_logits,
+    const float* A_log, const float* dt_bias, float lower_bound, float scale,
+    const void* initial_state, const int32_t* cu_seqlens, void* out, void* final_state,
+    void* workspace, void* stream, int64_t num_tokens, int32_t heads, int32_t num_seqs,
+    kda_state_dtype_t state_dtype, size_t workspace_bytes, const kda_strides_t* strides,
+    void* checkpoints, int32_t checkpoint_interval, int64_t checkpoint_capacity);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* kda_status_string(kda_status_t status);
 

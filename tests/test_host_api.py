@@ -31,7 +31,8 @@ def test_library_exports_every_declared_symbol():
     lib = kda.load_library()
     names = _declared_functions()
     assert set(names) == {"kda_get_workspace_size", "kda_chunk_prefill_fwd",
-                          "kda_chunk_prefill_fwd_strided", "kda_status_string",
+                          "kda_chunk_prefill_fwd_strided", "kda_chunk_prefill_fwd_checkpoints",
+                          "kda_status_string",
                           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/kda.h but not exported"
@@ -203,3 +204,36 @@ def test_debug_kernel_hook():
     assert lib.kda_debug_set_kernel(5) == -1
     assert lib.kda_debug_set_kernel(-1) == -1
     assert lib.kda_debug_set_kernel(0) == 0
+
+
+def _call_ck(ck=FAKE, interval=64, cap=256, **over):
+    """kda_chunk_prefill_fwd_checkpoints through ctypes (dense), valid-looking
+    defaults; every call below is rejected before any device access."""
+    lib = kda.load_library()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE,
+             lb=-5.0, scale=128 ** -0.5, s0=None, cu=FAKE, out=FAKE, sT=FAKE, ws=FAKE,
+             stream=None, T=16384, H=16, N=8, sdt=0, wsb=1 << 20)
+    a.update(over)
+    return lib.kda_chunk_prefill_fwd_checkpoints(
+        a["q"], a["k"], a["v"], a["g"], a["beta"], a["A_log"], a["dt_bias"], a["lb"],
+        a["scale"], a["s0"], a["cu"], a["out"], a["sT"], a["ws"], a["stream"], a["T"], a["H"],
+        a["N"], a["sdt"], a["wsb"], None, ck, interval, cap)
+
+
+@pytest.mark.parametrize("ck, interval, cap", [
+    (None, 64, 256),     # no checkpoint buffer
+    (FAKE, 0, 256), (FAKE, -64, 256), (FAKE, 40, 2 ** 20), (FAKE, 8, 2 ** 20),  # interval
+    (FAKE, 64, 255), (FAKE, 16, 1023),  # capacity below T / interval (16384 tokens)
+])
+def test_checkpoint_arguments_rejected(ck, interval, cap):
+    assert _call_ck(ck, interval, cap) == INVALID
+
+
+def test_checkpoints_below_pipelined_lower_bound_unsupported():
+    # lower_bound < -5 is served by the 64-token kernel, which writes no checkpoints
+    assert _call_ck(lb=-5.25) == UNSUPPORTED
+
+
+def test_checkpoints_keep_the_forward_checks():
+    assert _call_ck(q=None) == INVALID
+    assert _call_ck(wsb=0) == WS_SMALL
