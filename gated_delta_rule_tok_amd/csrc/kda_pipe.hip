@@ -210,14 +210,14 @@ struct RawLoad {
       r.k[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(src.k, col_off(t0, rr, ts_k), 0, 0));
     }
   }
-  // in the loop's issue order (rows, gate, q/k), which the scheduler must
+  // in the loop's issue order (gate, rows, q/k), which the scheduler must
   // keep: the waits at the top of the loop are computed over both ways in,
-  // so rows issued last here would make the first wait of every round drain
-  // the whole queue
+  // so a different order here would make the first waits of every round
+  // drain the whole queue
   __device__ __forceinline__ void all(Raw& r, int t0) const {
-    rows(r, t0);
-    __builtin_amdgcn_sched_barrier(0);
     gate(r, t0);
+    __builtin_amdgcn_sched_barrier(0);
+    rows(r, t0);
     __builtin_amdgcn_sched_barrier(0);
     qk(r, t0);
   }
@@ -287,23 +287,6 @@ __device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, Raw& raw,
                                                  const float* c2, float c1, float lb2, float scale) {
   const int cg = lane & 15, tq = lane >> 4;
 
-  // 1 / ||k_t|| and scale / ||q_t|| or beta_t for token lane/4 (beta: lane)
-  {
-    const float sk = row_norm2(raw.kn);
-    if ((lane & 3) == 0) pk.rk[hf][lane >> 2] = rsqrtf(sk + kNormEps);
-    if (hf) {
-      const float sq = row_norm2(raw.qn);
-      if ((lane & 3) == 0) pk.rqs[lane >> 2] = rsqrtf(sq + kNormEps) * scale;
-    } else if (lane < kTok) {
-      pk.beta[lane] = lane < Lc ? rcp(1.f + ex2(-kLog2e * bf16_to_f32(uint16_t(raw.beta)))) : 0.f;
-    }
-  }
-  // the next chunk's rows (tn), into the registers just consumed: they are
-  // the first thing the next round needs, so they get the longest lead
-  __builtin_amdgcn_sched_barrier(0);
-  ld.rows(raw, tn);
-  __builtin_amdgcn_sched_barrier(0);
-
   // gate sigma per (token, channel), its running sum over this lane's 4
   // tokens, then the sum over the earlier token groups (lanes 16 apart, by
   // lane permutes); the log2 decay of a token is lb2 * sigma (lb2 =
@@ -320,8 +303,26 @@ __device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, Raw& raw,
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  ld.gate(raw, tn);  // the next chunk's (tn), into the registers just consumed
+  // the next chunk's gate inputs (tn), into the registers just consumed:
+  // they are the first thing the next round needs, so they get the longest lead
+  ld.gate(raw, tn);
   __builtin_amdgcn_sched_barrier(0);
+  // 1 / ||k_t|| and scale / ||q_t|| or beta_t for token lane/4 (beta: lane)
+  {
+    const float sk = row_norm2(raw.kn);
+    if ((lane & 3) == 0) pk.rk[hf][lane >> 2] = rsqrtf(sk + kNormEps);
+    if (hf) {
+      const float sq = row_norm2(raw.qn);
+      if ((lane & 3) == 0) pk.rqs[lane >> 2] = rsqrtf(sq + kNormEps) * scale;
+    } else if (lane < kTok) {
+      pk.beta[lane] = lane < Lc ? rcp(1.f + ex2(-kLog2e * bf16_to_f32(uint16_t(raw.beta)))) : 0.f;
+    }
+  }
+  // the next chunk's rows (tn), into the registers just consumed
+  __builtin_amdgcn_sched_barrier(0);
+  ld.rows(raw, tn);
+  __builtin_amdgcn_sched_barrier(0);
+
   // the 4-token totals of the other token groups of this channel (rows of 16
   // lanes): permlane16_swap gives each lane its row pair's even and odd row,
   // permlane32_swap the two pairs' sums; no LDS round trip
