@@ -188,9 +188,9 @@ struct RawLoad {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       r.kn[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src.k, offk + 16u * i, 0, 0));
-      r.qn[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src.qn, offq + 16u * i, 0, 0));
+      if (hf) r.qn[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src.qn, offq + 16u * i, 0, 0));
     }
-    r.beta = __builtin_amdgcn_raw_buffer_load_b16(src.beta, (unsigned(t0) + unsigned(lane)) * unsigned(ts_b) * 2u, 0, 0);
+    if (!hf) r.beta = __builtin_amdgcn_raw_buffer_load_b16(src.beta, (unsigned(t0) + unsigned(lane)) * unsigned(ts_b) * 2u, 0, 0);
   }
   __device__ __forceinline__ unsigned col_off(int t0, int rr, int ts) const {
     const unsigned ch = 64u * unsigned(hf) + 4u * unsigned(lane & 15), tq = unsigned(lane >> 4);
@@ -572,11 +572,14 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   const int nc = (eos - bos + kTok - 1) / kTok;  // chunks
   const int nr = (nc + kPW - 1) / kPW;            // rounds
 
-  if (wave < kProdWaves) {
-    // ---------------- producer waves ----------------
-    // wave = chunk slot c of the round + kPW * channel half hf; the two
-    // waves of a chunk share a SIMD
-    const int c = wave & (kPW - 1), hf = wave / kPW;
+  // ---------------- producer waves ----------------
+  // wave = chunk slot c of the round + kPW * channel half hf; the two waves
+  // of a chunk share a SIMD.  One instance per half (hf known at compile
+  // time: the first half loads no q rows, the second no beta, with no
+  // branch around the loads)
+  auto producer = [&](auto half) {
+    constexpr int hf = decltype(half)::value;
+    const int c = wave & (kPW - 1);
     RawSrc src;
     src.q = rows_rsrc(p.q + size_t(h) * p.hs_q, eos, p.ts_q, kD);
     src.k = rows_rsrc(p.k + size_t(h) * p.hs_k, eos, p.ts_k, kD);
@@ -616,6 +619,10 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
       else produce_m(P, kg, lane);
       arrive(&sm.sy.rdy[r & 1][c], lane);
     }
+  };
+  if (wave < kProdWaves) {
+    if (wave < kPW) producer(BufIdx<0>{});
+    else producer(BufIdx<1>{});
     return;
   }
 
