@@ -1,0 +1,50 @@
+"""Host logic of bench.py: the algorithmic byte count behind the roofline and
+the conversion of rocprofv3 counter CSVs into HBM bytes per launch."""
+from __future__ import annotations
+
+import csv
+import os
+
+import bench
+
+
+def test_algorithmic_bytes_headline():
+    # 8 x 2048 tokens, 16 heads, fp32 state read and written:
+    # 16384 * 16 * (4 * 256 + 2 + 256) + 8 * 16 * 2 * 65536
+    assert bench.algorithmic_bytes(16384, 16, 8, 4, True) == 352_845_824
+    # no initial state: the state is only written; bf16 halves it
+    assert bench.algorithmic_bytes(16384, 16, 8, 4, False) == 16384 * 16 * 1282 + 8 * 16 * 65536
+    assert bench.algorithmic_bytes(256, 2, 1, 2, True) == 256 * 2 * 1282 + 2 * 2 * 32768
+
+
+def _write_counters(path, kernel, values_per_dispatch):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                           "Counter_Value"])
+        w.writeheader()
+        for d, vals in enumerate(values_per_dispatch):
+            for v in vals:  # several rows (e.g. per XCD) summed per dispatch
+                w.writerow(dict(Dispatch_Id=d, Kernel_Name=kernel, Counter_Name="X",
+                                Counter_Value=v))
+
+
+def test_traffic_from_counters(tmp_path):
+    pmc = str(tmp_path)
+    k = "void kda::(anonymous namespace)::pipe_kernel<64>(kda::Params)"
+    _write_counters(os.path.join(pmc, "fetch", "run_counter_collection.csv"), k,
+                    [[600.0, 400.0], [500.0, 500.0]])          # 1000 KiB per dispatch
+    _write_counters(os.path.join(pmc, "write", "run_counter_collection.csv"), k,
+                    [[250.0, 250.0]])                           # 500 KiB per dispatch
+    # the calibration copy of 256 MiB reads as half its bytes on FETCH_SIZE and
+    # all of them on WRITE_SIZE: scales x2 and x1
+    _write_counters(os.path.join(pmc, "cal_fetch", "run_counter_collection.csv"),
+                    "__amd_rocclr_copyBuffer", [[128 * 1024.0]])
+    _write_counters(os.path.join(pmc, "cal_write", "run_counter_collection.csv"),
+                    "__amd_rocclr_copyBuffer", [[256 * 1024.0]])
+    t = bench.traffic_from_pmc(pmc, "w", "cmd")
+    assert t["fetch_kib_per_dispatch"] == 1000.0 and t["write_kib_per_dispatch"] == 500.0
+    assert t["dispatches"] == [2, 1]
+    assert t["fetch_scale"] == 2.0 and t["write_scale"] == 1.0
+    assert t["bytes_per_launch"] == (1000.0 * 2.0 + 500.0) * 1024.0
+    assert t["kernel_source_sha256"] == bench.kernel_source_hash()
