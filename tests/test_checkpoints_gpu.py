@@ -118,3 +118,28 @@ def test_checkpoints_split_invariant():
     finally:
         kda.kda_debug_set_vsplit(0)
     assert all(torch.equal(res[0], r) for r in res[1:])
+
+
+@pytest.mark.parametrize("layout", ["fused_rows", "per_head"])
+def test_checkpoints_strided_match_dense_bitwise(layout):
+    """The checkpoint entry point on strided views (its strides argument)
+    gives the dense call's checkpoints, output and final state bit for bit."""
+    import torch
+    import gated_delta_rule_tok_amd as kda
+    from test_strided_gpu import _strided_views
+    x = KI.make_inputs([150, 66, 33, 1, 128], 3, seed=43, init_state="fp32")
+    d = to_device(x)
+    print(f"[case] checkpoints strided layout={layout} T={x.T} H={x.H}", flush=True)
+    out_d, fin_d, ck_d = _run_ck(x, d, 32, x.T // 32, 0)
+    sd, out_s, _ = _strided_views(d, layout)
+    _, fin_s, ws = alloc_outputs(x, d)
+    ck_s = torch.zeros_like(ck_d)
+    kda.kda_chunk_prefill_fwd(sd["q"], sd["k"], sd["v"], sd["g"], sd["beta"], d["A_log"],
+                              d["dt_bias"], x.lower_bound, x.scale, d["s0"], d["cu"], out_s,
+                              fin_s, ws, checkpoints=ck_s, checkpoint_interval=32)
+    torch.cuda.synchronize()
+    assert torch.equal(ck_s, ck_d)
+    assert torch.equal(fin_s, fin_d)
+    rows = torch.from_numpy(np.concatenate([np.arange(x.cu_seqlens[i], x.cu_seqlens[i + 1])
+                                            for i in range(x.N)])).to(out_d.device)
+    assert torch.equal(out_s[rows], out_d[rows])
