@@ -212,16 +212,24 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # the timed steps (value, ms_per_step): K calls back to back, nothing else
+    # queued between them
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # the same K calls again, each bracketed by events on its stream (per-launch
+    # durations for the roofline; the event records add small gaps between
+    # launches, which is why they are not in the loop above)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     for i in range(args.steps):
         ev[i][0].record(stream)
         step(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per_launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
 
     ms_per_step = wall * 1e3 / args.steps
