@@ -58,7 +58,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-KERNEL = "pipe_kernel"  # the dominant kernel of a call (the 16-token pipelined forward)
+KERNEL = "fwd32_kernel"  # the dominant kernel of a call (the 32-token pipelined forward)
 
 
 def traffic_file(workload: str) -> str:
@@ -180,7 +180,7 @@ def main():
         s = base if i == 0 else {k: (None if v is None else v.clone()) for k, v in base.items()}
         s["out"] = torch.empty(T, H, 128, dtype=torch.bfloat16, device=dev)
         s["fin"] = torch.empty(N, H, 128, 128, dtype=sdtype, device=dev)
-        s["ws"] = torch.empty(max(1, kda.kda_get_workspace_size(T, H, N)), dtype=torch.uint8,
+        s["ws"] = torch.zeros(max(1, kda.kda_get_workspace_size(T, H, N)), dtype=torch.uint8,
                               device=dev)
         s["ck"] = (torch.empty(T // args.checkpoint_interval, H, 128, 128, dtype=sdtype, device=dev)
                    if args.checkpoint_interval else None)

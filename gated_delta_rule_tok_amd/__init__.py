@@ -5,7 +5,7 @@ kernels behind the C ABI declared in include/kda.h.  Tensors are torch tensors
 used as device memory; the stream defaults to torch's current stream.  There
 is no CPU fallback: if libkda.so is missing, every call raises.
 
-    ws = torch.empty(kda_get_workspace_size(T, H, N), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(kda_get_workspace_size(T, H, N), dtype=torch.uint8, device="cuda")
     kda_chunk_prefill_fwd(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, scale,
                           initial_state, cu_seqlens, out, final_state, ws)
 
@@ -19,7 +19,8 @@ import ctypes
 import os
 
 __all__ = ["kda_get_workspace_size", "kda_chunk_prefill_fwd", "kda_status_string",
-           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel", "KdaError", "library_path", "load_library"]
+           "kda_workspace_status",
+           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel", "kda_debug_set_share", "KdaError", "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -93,12 +94,22 @@ def load_library():
         lib.kda_debug_set_kernel.restype = ctypes.c_int
         lib.kda_debug_set_vsplit.argtypes = [ctypes.c_int]
         lib.kda_debug_set_vsplit.restype = ctypes.c_int
+        lib.kda_debug_set_share.argtypes = [ctypes.c_int]
+        lib.kda_debug_set_share.restype = ctypes.c_int
         _lib = lib
     return _lib
 
 
 def kda_get_workspace_size(max_tokens: int, heads: int, max_seqs: int) -> int:
     return int(load_library().kda_get_workspace_size(int(max_tokens), int(heads), int(max_seqs)))
+
+
+def kda_workspace_status(workspace) -> int:
+    """The workspace's status word (its first 4 bytes, see include/kda.h): 0 while
+    every call that used it ran to completion normally; 1 once a kernel gave up
+    a bounded wait (the outputs of that call are void).  Synchronises the device."""
+    import torch
+    return int(workspace[:4].view(torch.int32)[0].item())
 
 
 def kda_status_string(status: int) -> str:
@@ -124,6 +135,15 @@ def kda_debug_set_vsplit(s: int) -> int:
     prev = load_library().kda_debug_set_vsplit(int(s))
     if prev < 0:
         raise ValueError(f"invalid value split {s}")
+    return prev
+
+
+def kda_debug_set_share(mode: int) -> int:
+    """Test hook: 0 automatic (default), 1 the two workgroups of a value split
+    of two never share chunk packages (each builds every chunk itself)."""
+    prev = load_library().kda_debug_set_share(int(mode))
+    if prev < 0:
+        raise ValueError(f"invalid share mode {mode}")
     return prev
 
 

@@ -9,6 +9,7 @@
 // state dtype and the workspace capacity added so a C caller can be checked.
 // Failing fast on a bad configuration follows the same page's backend
 // resolver ("Implementation breakdown", item 1).
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -23,12 +24,19 @@ constexpr size_t kAlign = 256;
 constexpr int kMaxDevices = 64;
 
 std::atomic<int> g_vsplit_override{0};
+std::atomic<int> g_share_override{0};
 std::atomic<int> g_kernel_override{0};
 std::atomic<int> g_cu_count[kMaxDevices];
 
 thread_local char t_last_hip_error[256] = "";
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// ring space for the first kFwdShareItems items (grids above that size never
+// share; the bound keeps the size monotone in heads and sequences)
+size_t share_bytes(int64_t items) {
+  return size_t(std::min<int64_t>(items, kda::kFwdShareItems)) * (kda::kFwdCtlBytes + kda::kFwdRingBytes);
+}
 
 kda_status_t hip_failure(hipError_t e, const char* step) {
   std::snprintf(t_last_hip_error, sizeof t_last_hip_error, "%s (%s) during %s", hipGetErrorName(e),
@@ -74,8 +82,10 @@ extern "C" {
 
 size_t kda_get_workspace_size(int64_t max_tokens, int32_t heads, int32_t max_seqs) {
   if (max_tokens < 0 || heads <= 0 || max_seqs <= 0) return 0;
-  // sequence order table (longest first)
-  return align_up(sizeof(int32_t) * size_t(max_seqs));
+  // status word (padded to kAlign), the sequence order table (longest first),
+  // and the control words and package ring through which the two workgroups
+  // of a value split of two share the chunk packages
+  return kAlign + align_up(sizeof(int32_t) * size_t(max_seqs)) + share_bytes(int64_t(heads) * max_seqs);
 }
 
 const char* kda_status_string(kda_status_t status) {
@@ -93,9 +103,15 @@ const char* kda_last_hip_error(void) { return t_last_hip_error; }
 
 int kda_debug_set_kernel(int k) {
   // 0 automatic, 1 64-token chunk, 2 token-serial, 3 token-serial decode
-  // staging (4 tokens), 4 pipelined 16-token
-  if (k < 0 || k > 4) return -1;
+  // staging (4 tokens), 4 pipelined 16-token, 5 pipelined 32-token
+  if (k < 0 || k > 5) return -1;
   return g_kernel_override.exchange(k);
+}
+
+int kda_debug_set_share(int mode) {
+  // 0 automatic, 1 never share packages between the workgroups of a value split
+  if (mode < 0 || mode > 1) return -1;
+  return g_share_override.exchange(mode);
 }
 
 int kda_debug_set_vsplit(int s) {
@@ -151,7 +167,6 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   if (checkpoints) {
     if (ck_interval <= 0 || ck_interval % 16) return KDA_ERR_INVALID_ARG;
     if (ck_capacity < num_tokens / ck_interval) return KDA_ERR_INVALID_ARG;
-    if (lower_bound < kda::kPipeLowerBoundMin) return KDA_ERR_UNSUPPORTED;
   }
   const size_t need = kda_get_workspace_size(num_tokens, heads, num_seqs);
   if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
@@ -175,7 +190,10 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   p.sT = final_state;
   p.out = static_cast<uint16_t*>(out);
   p.cu = cu_seqlens;
-  p.order = static_cast<int32_t*>(workspace);
+  p.errword = static_cast<int32_t*>(workspace);
+  p.order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kAlign);
+  p.ring = nullptr;
+  p.ring_ctl = nullptr;
   p.lower_bound = lower_bound;
   p.scale = scale;
   p.ts_q = int(sd.q_token), p.hs_q = int(sd.q_head);
@@ -194,24 +212,35 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   p.ck_cap = ck_capacity;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // the pipelined kernel takes lower_bound >= -5 and slices of <= 64 value
-  // columns; anything else (or the test override) goes to the 64-token kernel
+  // kernel families: 5 the pipelined 32-token kernel (default), 3 the decode
+  // kernel for decode-sized calls (at most kDecodeTokensPerSeq tokens per
+  // sequence on average: it streams each state once with 16-byte accesses and
+  // the chunked machinery does not pay off), 1, 2, 4 on request (test hook)
   const int override = g_kernel_override.load(std::memory_order_relaxed);
-  int kernel = override == 4 ? 0 : override;
-  // decode-sized calls (at most kDecodeTokensPerSeq tokens per sequence on
-  // average): the decode kernel streams each state once with 16-byte
-  // accesses; the chunked kernels' machinery does not pay off there
-  if (override == 0 && num_tokens <= kda::kDecodeTokensPerSeq * int64_t(num_seqs)) kernel = 3;
-  // checkpoints: the pipelined kernel only, whatever the call's size
-  if (checkpoints && override == 0) kernel = 0;
-  if (kernel == 0 && lower_bound < kda::kPipeLowerBoundMin) kernel = 1;
-  if (kernel == 0 && p.vsplit == 1) p.vsplit = forced > 0 ? 1 : 2;
-  if (kernel == 0 && p.vsplit == 1) kernel = 1;
-  if (checkpoints && kernel != 0) return KDA_ERR_UNSUPPORTED;
-  // the sequence order table (longest first): the pipelined kernel ranks a
-  // few sequences itself, the decode path takes them in index order, the
+  int kernel = override;
+  if (kernel == 0)
+    kernel = (!checkpoints && num_tokens <= kda::kDecodeTokensPerSeq * int64_t(num_seqs)) ? 3 : 5;
+  // the 16-token kernel takes lower_bound >= -5 and slices of <= 64 value
+  // columns; anything else goes to the 64-token kernel
+  if (kernel == 4 && lower_bound < kda::kPipeLowerBoundMin) kernel = 1;
+  if (kernel == 4 && p.vsplit == 1) p.vsplit = forced > 0 ? 1 : 2;
+  if (kernel == 4 && p.vsplit == 1) kernel = 1;
+  if (checkpoints && kernel != 4 && kernel != 5) return KDA_ERR_UNSUPPORTED;
+  // value split of two on the 32-token kernel: the two workgroups of each
+  // (sequence, head) build alternate chunks and exchange them through the
+  // workspace ring, when the whole grid is resident at once (it fits the
+  // compute units) and maps the pair onto one XCD (a multiple of 16)
+  const int64_t items = int64_t(num_seqs) * heads;
+  if (kernel == 5 && p.vsplit == 2 && items <= kda::kFwdShareItems && 2 * items <= cus &&
+      (2 * items) % 16 == 0 && g_share_override.load(std::memory_order_relaxed) == 0) {
+    char* base = static_cast<char*>(workspace) + kAlign + align_up(sizeof(int32_t) * size_t(num_seqs));
+    p.ring_ctl = reinterpret_cast<int32_t*>(base);
+    p.ring = reinterpret_cast<uint8_t*>(base + size_t(items) * kda::kFwdCtlBytes);
+  }
+  // the sequence order table (longest first): the pipelined kernels rank a
+  // few sequences themselves, the decode path takes them in index order, the
   // others read the table
-  if ((kernel == 0 && num_seqs <= kda::kInlineRankMax) || kernel == 3) {
+  if (((kernel == 4 || kernel == 5) && num_seqs <= kda::kInlineRankMax) || kernel == 3) {
     p.order = nullptr;
   } else if (hipError_t e = kda::launch_plan(p, st); e != hipSuccess) {
     return hip_failure(e, "plan launch");
@@ -222,9 +251,12 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   } else if (kernel == 1) {
     if (hipError_t e = kda::launch_chunk(p, st); e != hipSuccess)
       return hip_failure(e, "64-token chunk kernel launch");
-  } else {
+  } else if (kernel == 4) {
     if (hipError_t e = kda::launch_pipe(p, st); e != hipSuccess)
-      return hip_failure(e, "pipelined chunk kernel launch");
+      return hip_failure(e, "pipelined 16-token kernel launch");
+  } else {
+    if (hipError_t e = kda::launch_fwd32(p, st); e != hipSuccess)
+      return hip_failure(e, "pipelined 32-token kernel launch");
   }
   return KDA_OK;
 }

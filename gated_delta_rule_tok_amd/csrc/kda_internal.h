@@ -26,7 +26,15 @@ struct Params {
   uint16_t* out;
   const int32_t* cu;
   int32_t* order;  // sequence processing order (longest first), [N], in the workspace;
-                   // null: the kernel ranks the sequences itself (pipelined kernel, N small)
+                   // null: the kernel ranks the sequences itself (pipelined kernels, N small)
+  int32_t* errword;  // the workspace's status word: a kernel sets it to 1 if a bounded
+                     // wait gave up (never cleared here)
+  // 32-token kernel with a value split of two: the two workgroups of a
+  // (sequence, head) share the chunk packages through these (null: each
+  // builds every chunk).  ring_ctl: kFwdCtlBytes per item, zero between calls;
+  // ring: kFwdRingBytes per item.  Items are sequence * H + head, < kFwdShareItems.
+  uint8_t* ring;
+  int32_t* ring_ctl;
   float lower_bound;
   float scale;
   // element strides of the per-token tensors (channels contiguous): row
@@ -65,11 +73,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // Workgroup index B of a grid of G -> work item b = rank * s + slice (s value
-// slices per (sequence rank, head) item).  Workgroup B runs on XCD B mod 8, so
-// items are handed out in rank order across the 8 XCDs (ranked, longest-first
-// work spreads evenly over them) and the s slices of one item sit on one XCD,
-// 8 workgroup indices apart, sharing q/k/g in its L2.  Identity when G is not
-// a multiple of 8 s.
+// slices per (sequence rank, head) item).  The dispatcher hands workgroups to
+// the 8 XCDs round robin (B on XCD (B + o) mod 8; the offset o depends on where
+// the previous dispatch ended), so items are handed out in rank order across
+// the XCDs (ranked, longest-first work spreads evenly over them) and the s
+// slices of one item sit on one XCD, 8 workgroup indices apart, sharing q/k/g
+// in its L2.  Identity when G is not a multiple of 8 s.
 __device__ __forceinline__ int work_item(int B, int G, int s) {
   if (G % (8 * s)) return B;
   const int xcd = B & 7, k = B >> 3;
@@ -104,5 +113,15 @@ constexpr float kPipeLowerBoundMin = -5.0f;
 constexpr int kDecodeTokensPerSeq = 8;
 constexpr int kInlineRankMax = 16;
 hipError_t launch_pipe(const Params& p, hipStream_t stream);
+
+// Pipelined 32-token chunk forward (two 16-token halves with their own decay
+// reference points): four producer waves build the packages of alternating
+// chunks, the state waves walk them in order.  Any value slice of 16..128
+// columns, lower_bound in [-5.5, 0].  Ranks up to kInlineRankMax sequences
+// itself.
+hipError_t launch_fwd32(const Params& p, hipStream_t stream);
+constexpr int kFwdShareItems = 128;            // (sequence, head) items with a shared ring
+constexpr size_t kFwdCtlBytes = 256;           // control words per item
+constexpr size_t kFwdRingBytes = 4 * 30720;    // package images per item (2 slices x 2 slots)
 
 }  // namespace kda

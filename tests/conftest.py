@@ -18,3 +18,12 @@ def oracle_mod():
     import oracle
     oracle.build(force=False)
     return oracle
+
+
+@pytest.fixture(autouse=True)
+def _workspace_status(request):
+    """GPU tests: every workspace's status word is still 0 after the test."""
+    yield
+    if request.node.get_closest_marker("gpu") is not None:
+        from gpu_util import check_workspaces
+        check_workspaces()

@@ -48,9 +48,34 @@ def alloc_outputs(x: KI.KdaInputs, d, fill_out=None):
     if fill_out is not None:
         out.view(torch.int16).fill_(fill_out)
     fin = torch.empty(x.N, x.H, 128, 128, dtype=d["state_dtype"], device=dev)
-    ws = torch.empty(max(1, kda.kda_get_workspace_size(x.T, x.H, x.N)), dtype=torch.uint8,
-                     device=dev)
+    ws = new_workspace(x.T, x.H, x.N, dev)
     return out, fin, ws
+
+
+# Every workspace the GPU tests hand to the library: its status word (the
+# first 4 bytes) must still be zero when the test ends (no kernel gave up a
+# bounded wait).  Checked by the autouse fixture in conftest.py.
+_workspaces = []
+
+
+def new_workspace(T, H, N, device="cuda"):
+    import torch
+    import gated_delta_rule_tok_amd as kda
+    ws = torch.zeros(max(1, kda.kda_get_workspace_size(T, H, N)), dtype=torch.uint8, device=device)
+    _workspaces.append(ws)
+    return ws
+
+
+def check_workspaces():
+    """Assert the status word of every workspace used since the last check is 0."""
+    import torch
+    import gated_delta_rule_tok_amd as kda
+    if not _workspaces:
+        return
+    torch.cuda.synchronize()
+    bad = [kda.kda_workspace_status(ws) for ws in _workspaces]
+    _workspaces.clear()
+    assert not any(bad), f"a kernel gave up a bounded wait (status words {bad})"
 
 
 def run_gpu(x: KI.KdaInputs, d, out=None, fin=None, ws=None, s0="default", stream=None):

@@ -33,7 +33,8 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == {"kda_get_workspace_size", "kda_chunk_prefill_fwd",
                           "kda_chunk_prefill_fwd_strided", "kda_chunk_prefill_fwd_checkpoints",
                           "kda_status_string",
-                          "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel"}
+                          "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel",
+                          "kda_debug_set_share"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/kda.h but not exported"
 
@@ -199,9 +200,9 @@ def test_python_binding_strided_views_keep_channel_contiguity():
 
 def test_debug_kernel_hook():
     lib = kda.load_library()
-    for k in (1, 2, 3, 4, 0):
+    for k in (1, 2, 3, 4, 5, 0):
         assert lib.kda_debug_set_kernel(k) >= 0
-    assert lib.kda_debug_set_kernel(5) == -1
+    assert lib.kda_debug_set_kernel(6) == -1
     assert lib.kda_debug_set_kernel(-1) == -1
     assert lib.kda_debug_set_kernel(0) == 0
 
@@ -229,9 +230,10 @@ def test_checkpoint_arguments_rejected(ck, interval, cap):
     assert _call_ck(ck, interval, cap) == INVALID
 
 
-def test_checkpoints_below_pipelined_lower_bound_unsupported():
-    # lower_bound < -5 is served by the 64-token kernel, which writes no checkpoints
-    assert _call_ck(lb=-5.25) == UNSUPPORTED
+def test_checkpoints_below_lower_bound_min_unsupported():
+    # the checkpoint call keeps the forward's lower_bound range [-5.5, 0]
+    assert _call_ck(lb=-5.75) == UNSUPPORTED
+    assert _call_ck(lb=0.5) == UNSUPPORTED
 
 
 def test_checkpoints_keep_the_forward_checks():
