@@ -58,7 +58,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-KERNEL = "fwd32_kernel"  # the dominant kernel of a call (the 32-token pipelined forward)
+KERNEL = "pipe_kernel"  # the dominant kernel of a call (the 16-token pipelined forward)
 
 
 def traffic_file(workload: str) -> str:

@@ -20,7 +20,7 @@ import os
 
 __all__ = ["kda_get_workspace_size", "kda_chunk_prefill_fwd", "kda_status_string",
            "kda_workspace_status",
-           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel", "kda_debug_set_share", "KdaError", "library_path", "load_library"]
+           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel", "KdaError", "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -94,8 +94,6 @@ def load_library():
         lib.kda_debug_set_kernel.restype = ctypes.c_int
         lib.kda_debug_set_vsplit.argtypes = [ctypes.c_int]
         lib.kda_debug_set_vsplit.restype = ctypes.c_int
-        lib.kda_debug_set_share.argtypes = [ctypes.c_int]
-        lib.kda_debug_set_share.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -135,15 +133,6 @@ def kda_debug_set_vsplit(s: int) -> int:
     prev = load_library().kda_debug_set_vsplit(int(s))
     if prev < 0:
         raise ValueError(f"invalid value split {s}")
-    return prev
-
-
-def kda_debug_set_share(mode: int) -> int:
-    """Test hook: 0 automatic (default), 1 the two workgroups of a value split
-    of two never share chunk packages (each builds every chunk itself)."""
-    prev = load_library().kda_debug_set_share(int(mode))
-    if prev < 0:
-        raise ValueError(f"invalid share mode {mode}")
     return prev
 
 

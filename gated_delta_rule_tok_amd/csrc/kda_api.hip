@@ -9,7 +9,6 @@
 // state dtype and the workspace capacity added so a C caller can be checked.
 // Failing fast on a bad configuration follows the same page's backend
 // resolver ("Implementation breakdown", item 1).
-#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -24,19 +23,12 @@ constexpr size_t kAlign = 256;
 constexpr int kMaxDevices = 64;
 
 std::atomic<int> g_vsplit_override{0};
-std::atomic<int> g_share_override{0};
 std::atomic<int> g_kernel_override{0};
 std::atomic<int> g_cu_count[kMaxDevices];
 
 thread_local char t_last_hip_error[256] = "";
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-
-// ring space for the first kFwdShareItems items (grids above that size never
-// share; the bound keeps the size monotone in heads and sequences)
-size_t share_bytes(int64_t items) {
-  return size_t(std::min<int64_t>(items, kda::kFwdShareItems)) * (kda::kFwdCtlBytes + kda::kFwdRingBytes);
-}
 
 kda_status_t hip_failure(hipError_t e, const char* step) {
   std::snprintf(t_last_hip_error, sizeof t_last_hip_error, "%s (%s) during %s", hipGetErrorName(e),
@@ -82,10 +74,8 @@ extern "C" {
 
 size_t kda_get_workspace_size(int64_t max_tokens, int32_t heads, int32_t max_seqs) {
   if (max_tokens < 0 || heads <= 0 || max_seqs <= 0) return 0;
-  // status word (padded to kAlign), the sequence order table (longest first),
-  // and the control words and package ring through which the two workgroups
-  // of a value split of two share the chunk packages
-  return kAlign + align_up(sizeof(int32_t) * size_t(max_seqs)) + share_bytes(int64_t(heads) * max_seqs);
+  // status word (padded to kAlign), then the sequence order table (longest first)
+  return kAlign + align_up(sizeof(int32_t) * size_t(max_seqs));
 }
 
 const char* kda_status_string(kda_status_t status) {
@@ -106,12 +96,6 @@ int kda_debug_set_kernel(int k) {
   // staging (4 tokens), 4 pipelined 16-token, 5 pipelined 32-token
   if (k < 0 || k > 5) return -1;
   return g_kernel_override.exchange(k);
-}
-
-int kda_debug_set_share(int mode) {
-  // 0 automatic, 1 never share packages between the workgroups of a value split
-  if (mode < 0 || mode > 1) return -1;
-  return g_share_override.exchange(mode);
 }
 
 int kda_debug_set_vsplit(int s) {
@@ -192,8 +176,6 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   p.cu = cu_seqlens;
   p.errword = static_cast<int32_t*>(workspace);
   p.order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kAlign);
-  p.ring = nullptr;
-  p.ring_ctl = nullptr;
   p.lower_bound = lower_bound;
   p.scale = scale;
   p.ts_q = int(sd.q_token), p.hs_q = int(sd.q_head);
@@ -212,31 +194,26 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   p.ck_cap = ck_capacity;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // kernel families: 5 the pipelined 32-token kernel (default), 3 the decode
-  // kernel for decode-sized calls (at most kDecodeTokensPerSeq tokens per
-  // sequence on average: it streams each state once with 16-byte accesses and
-  // the chunked machinery does not pay off), 1, 2, 4 on request (test hook)
+  // kernel families: 4 the pipelined 16-token kernel (default for
+  // lower_bound >= kPipeLowerBoundMin), 5 the pipelined 32-token kernel (its
+  // two 16-token halves keep their own decay references, so it serves
+  // lower_bound down to KDA_LOWER_BOUND_MIN), 3 the decode kernel for
+  // decode-sized calls (at most kDecodeTokensPerSeq tokens per sequence on
+  // average: it streams each state once with 16-byte accesses and the chunked
+  // machinery does not pay off), 1 and 2 on request (test hook)
   const int override = g_kernel_override.load(std::memory_order_relaxed);
   int kernel = override;
   if (kernel == 0)
-    kernel = (!checkpoints && num_tokens <= kda::kDecodeTokensPerSeq * int64_t(num_seqs)) ? 3 : 5;
+    kernel = (!checkpoints && num_tokens <= kda::kDecodeTokensPerSeq * int64_t(num_seqs)) ? 3 : 4;
   // the 16-token kernel takes lower_bound >= -5 and slices of <= 64 value
-  // columns; anything else goes to the 64-token kernel
-  if (kernel == 4 && lower_bound < kda::kPipeLowerBoundMin) kernel = 1;
-  if (kernel == 4 && p.vsplit == 1) p.vsplit = forced > 0 ? 1 : 2;
+  // columns: below that bound the 32-token kernel, an unsplit launch (test
+  // hook) the 64-token kernel.  Both pipelined kernels split the value
+  // dimension at least in two when the rule says unsplit (a 128-column slice
+  // holds more state than their waves' registers: measured slower)
+  if (kernel == 4 && lower_bound < kda::kPipeLowerBoundMin) kernel = 5;
+  if ((kernel == 4 || kernel == 5) && p.vsplit == 1 && forced == 0) p.vsplit = 2;
   if (kernel == 4 && p.vsplit == 1) kernel = 1;
   if (checkpoints && kernel != 4 && kernel != 5) return KDA_ERR_UNSUPPORTED;
-  // value split of two on the 32-token kernel: the two workgroups of each
-  // (sequence, head) build alternate chunks and exchange them through the
-  // workspace ring, when the whole grid is resident at once (it fits the
-  // compute units) and maps the pair onto one XCD (a multiple of 16)
-  const int64_t items = int64_t(num_seqs) * heads;
-  if (kernel == 5 && p.vsplit == 2 && items <= kda::kFwdShareItems && 2 * items <= cus &&
-      (2 * items) % 16 == 0 && g_share_override.load(std::memory_order_relaxed) == 0) {
-    char* base = static_cast<char*>(workspace) + kAlign + align_up(sizeof(int32_t) * size_t(num_seqs));
-    p.ring_ctl = reinterpret_cast<int32_t*>(base);
-    p.ring = reinterpret_cast<uint8_t*>(base + size_t(items) * kda::kFwdCtlBytes);
-  }
   // the sequence order table (longest first): the pipelined kernels rank a
   // few sequences themselves, the decode path takes them in index order, the
   // others read the table

@@ -324,8 +324,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(Params p) {
       }
   }
 
-  const int bos = min(max(p.cu[n], 0), p.T);
-  const int eos = min(max(p.cu[n + 1], bos), p.T);
+  // the bounds are uniform: scalar registers (else every buffer access with a
+  // token offset in its scalar operand becomes a loop over lanes)
+  const int bos = __builtin_amdgcn_readfirstlane(min(max(p.cu[n], 0), p.T));
+  const int eos = __builtin_amdgcn_readfirstlane(min(max(p.cu[n + 1], bos), p.T));
 
   // base pointers of token 0 for this head (and this thread's channels);
   // per-token offsets below are 32-bit ((T + 256) * stride < 2^31 elements is

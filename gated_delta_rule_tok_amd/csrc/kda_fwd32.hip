@@ -62,7 +62,6 @@ constexpr int kSpinMax = 1 << 22;  // polls before a wait gives up (then the err
 // lies in [2^-119, 2^119], so none is a denormal (which the hardware flushes:
 // e^{G_t} of a half's last token and its K_G partner meet in M's diagonal).
 constexpr float kShift = 8.f;
-constexpr int kSc1 = 16;  // buffer cache policy: device scope (loads miss the L1 and read the L2)
 constexpr float kSDown = 1.f / 256.f;  // state held as 2^-8 S
 constexpr float kSUp = 256.f;
 
@@ -111,20 +110,11 @@ struct Pack {
   float gam[2][128];       // Gam_0, Gam_1 (gmo order)
   float b16[kC];           // b / 16
   float rqs[kC];           // scale / |q|
-  int pad[192];            // to a whole number of kilobytes (copied between workgroups in 1 KB blocks)
 };
-constexpr int kPackBytes = 30720;
-constexpr int kPackBlocks = kPackBytes / 1024;
-static_assert(sizeof(Pack) == kPackBytes, "package image size");
 
 struct Scratch {           // per slot, read only by the products of the same chunk
   bf16 kg[kC * 128];       // 2^-8 K_G^h, token rows (tro)
   bf16 kp0[kHT * 128];     // bf16(K'^0 / 16), token rows (tro)
-};
-
-// Partial squared norms of one chunk slot's half: [channel half][token][k, q]
-struct Norms {
-  float kq[2][kHT][2];
 };
 
 // Per state wave and strip: V rows -> accumulator layout, O accumulator ->
@@ -137,13 +127,9 @@ struct Tile {
 // LDS counters, all counted over the run (so a count names a chunk).
 struct Sync {
   int done[kSlots][4];   // per state wave: chunks of this slot it is done with
-  int nrm[kSlots][2];    // per (slot, half): partial norms written (two per chunk)
-  int opnd[kSlots];      // per slot: quarters whose operands are in LDS (four per chunk)
-  int rdy[kSlots][2];    // per package buffer: four per complete package (products: 2 + 2;
-                         // received from the partner workgroup: 1 per producer wave)
-  int pdone;             // producer waves finished
+  int opnd[kSlots];      // per producer slot: halves whose operands are in LDS (two per chunk)
+  int rdy[kSlots][2];    // per package buffer: four per complete package (products: 2 + 2)
   int err;               // a bounded wait gave up (its kind)
-  int mode;              // with a ring: 1 share packages with the partner, 2 build every chunk
   int pad;
 };
 
@@ -151,7 +137,6 @@ template <int NSW, int SPW>
 struct Smem {
   Pack pk[kSlots][2];
   Scratch sc[kSlots];
-  Norms nr[kSlots][2];
   Tile tl[NSW][SPW];
   Sync sy;
 };
@@ -171,8 +156,7 @@ __device__ __forceinline__ bool gave_up(const int* err) {
   return __builtin_amdgcn_readfirstlane(__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != 0;
 }
 // Record a give-up: the first one's kind stays (status word values).
-constexpr int kErrWait = 1;     // a wait on this workgroup's LDS counters
-constexpr int kErrPartner = 2;  // a wait on the partner workgroup's words
+constexpr int kErrWait = 1;  // a wait on this workgroup's LDS counters
 __device__ __forceinline__ void give_up(int* err, int code) {
   int expected = 0;
   __hip_atomic_compare_exchange_strong(err, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
@@ -213,90 +197,6 @@ __device__ __forceinline__ void wait_row(const int* row, int target, int* err) {
 // Add n to an LDS counter (release).
 __device__ __forceinline__ void arrive_n(int* ctr, int lane, int n) {
   if (lane == 0) __hip_atomic_fetch_add(ctr, n, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-// Wait until at most N vector memory operations of this wave are outstanding
-// (they complete in issue order): an explicit count, so that a wait for old
-// stores or loads does not also wait for the loads issued after them.
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// ---- exchange between the two value slices of a (sequence, head) ---------------
-// With a value split of two, the two workgroups of a (sequence, head) run on
-// one XCD (work_item) and share its L2.  Each builds the packages of every
-// other chunk and hands them to the other through a ring in the workspace:
-// per item, [publishing slice][slot] images of kPackBytes, and 64 control
-// words: flag[pub][slot][quarter] = chunk + 1 once that quarter of the image
-// is stored, a count of finished workgroups (the second resets the item's
-// words to zero for the next call) and each workgroup's XCD (+ 1).  Blocks B
-// and B + 8 run on one XCD when the dispatcher hands out workgroups round
-// robin over the eight XCDs, whatever XCD it starts the grid on; the two
-// workgroups check it (each publishes its XCD and reads the other's) and
-// otherwise both build every chunk themselves.
-//
-// A slot is free again without an acknowledgement: a wave publishes its chunk
-// of round r (slot r & 1) after it has seen the partner's flag for the
-// partner's chunk of round r - 1, which the partner raises only after its
-// copy of this wave's chunk of round r - 2 (the slot's previous image) is in
-// its LDS.
-constexpr int kRing = 2;
-constexpr int kCtlInts = 64;
-constexpr int kCtlDone = 16;
-constexpr int kCtlXcc = 17;   // [slice]
-constexpr int kCtlUsed = 19;  // words reset at the end
-
-// Scalar load of a global word that bypasses the scalar cache (glc), waited
-// for in the same statement.  Used for polling: it does not touch the vector
-// memory counter, so the wave's in-flight loads are not waited for.
-__device__ __forceinline__ int sload_glc(const int* p) {
-  // the address is uniform; make it a scalar register pair for the compiler too
-  const unsigned long long a = reinterpret_cast<unsigned long long>(p);
-  const unsigned lo = __builtin_amdgcn_readfirstlane(unsigned(a)), hi = __builtin_amdgcn_readfirstlane(unsigned(a >> 32));
-  const int* ps = reinterpret_cast<const int*>((static_cast<unsigned long long>(hi) << 32) | lo);
-  int v;
-  asm volatile("s_load_dword %0, %1, 0x0 glc\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ps) : "memory");
-  return v;
-}
-__device__ __forceinline__ void poll_global(const int* p, int target, int* err) {
-  if (gave_up(err)) return;
-#pragma unroll 1
-  for (int it = 0; it < kSpinMax; ++it) {
-    if (sload_glc(p) >= target) return;
-    __builtin_amdgcn_s_sleep(2);
-  }
-  give_up(err, kErrPartner);
-}
-__device__ __forceinline__ void store_global(int* p, int v, int lane) {
-  if (lane == 0) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Package image blocks (1 KB) of producer wave Q: Q, Q + 4, ..
-template <int Q>
-constexpr int nblocks() { return (kPackBlocks - Q + 3) / 4; }
-
-// LDS package -> ring image (wave Q's blocks)
-template <int Q>
-__device__ __forceinline__ void publish(const Pack& P, __amdgpu_buffer_rsrc_t ring, unsigned soff, int lane) {
-  const char* base = reinterpret_cast<const char*>(&P);
-  typedef int i32x4v __attribute__((ext_vector_type(4)));
-#pragma unroll
-  for (int b = Q; b < kPackBlocks; b += 4) {
-    const i32x4v v = *reinterpret_cast<const i32x4v*>(base + b * 1024 + lane * 16);
-    __builtin_amdgcn_raw_buffer_store_b128(v, ring, unsigned(lane) * 16u, soff + unsigned(b) * 1024u, 0);
-  }
-}
-// ring image -> LDS package (wave Q's blocks), straight into LDS (no
-// registers); complete when the wave's vector memory count says so
-template <int Q>
-__device__ __forceinline__ void receive(Pack& P, __amdgpu_buffer_rsrc_t ring, unsigned soff, int lane) {
-  char* base = reinterpret_cast<char*>(&P);
-#pragma unroll
-  for (int b = Q; b < kPackBlocks; b += 4)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ring, (__attribute__((address_space(3))) void*)(base + b * 1024), 16,
-                                             unsigned(lane) * 16u, soff + unsigned(b) * 1024u, 0, kSc1);
 }
 
 // ---- small helpers --------------------------------------------------------------
@@ -352,13 +252,13 @@ __device__ __forceinline__ f32x4 mfma16x(f16x4 a, f16x4 b, f32x4 c) {
 }
 
 // ---- producer: raw loads ----------------------------------------------------------
-// One quarter of a chunk per producer wave (a half of 16 tokens x a channel
-// half of 64): lane (tq = lane / 16, cg = lane % 16) holds tokens 4 tq + i
-// (i = 0..3) of the half, channels 64 CH + 4 cg .. + 3, so 16 consecutive
-// lanes read one 128-byte row segment.  The per-chunk part of each byte offset
-// is a scalar (soffset); the lane part is fixed.
+// One half of a chunk (16 tokens, all 128 channels) per producer wave: lane
+// (tq = lane / 16, cg = lane % 16) holds tokens 4 tq + i (i = 0..3) of the
+// half, channels 8 cg .. + 7 (one 16-byte unit), so 16 consecutive lanes read
+// one 256-byte row.  The per-chunk part of each byte offset is a scalar
+// (soffset); the lane part is fixed.
 struct Raw {
-  uint2 q[4], k[4], g[4];
+  uint4 q[4], k[4], g[4];
   uint32_t beta;
 };
 
@@ -366,84 +266,69 @@ struct Loader {
   __amdgpu_buffer_rsrc_t q, k, g, beta;
   unsigned vq, vk, vg, vb;  // lane parts of the byte offsets
   int ts_q, ts_k, ts_g, ts_b;
-  __device__ __forceinline__ void init(int lane, int ch0) {
+  __device__ __forceinline__ void init(int lane) {
     const unsigned tq = unsigned(lane >> 4), cg = unsigned(lane & 15);
-    vq = (4u * tq * unsigned(ts_q) + unsigned(ch0) + 4u * cg) * 2u;
-    vk = (4u * tq * unsigned(ts_k) + unsigned(ch0) + 4u * cg) * 2u;
-    vg = (4u * tq * unsigned(ts_g) + unsigned(ch0) + 4u * cg) * 2u;
+    vq = (4u * tq * unsigned(ts_q) + 8u * cg) * 2u;
+    vk = (4u * tq * unsigned(ts_k) + 8u * cg) * 2u;
+    vg = (4u * tq * unsigned(ts_g) + 8u * cg) * 2u;
     vb = cg * unsigned(ts_b) * 2u;
   }
   __device__ __forceinline__ void gate(Raw& r, int t0) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      r.g[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(g, vg, (unsigned(t0) + i) * unsigned(ts_g) * 2u, 0));
+      r.g[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(g, vg, (unsigned(t0) + i) * unsigned(ts_g) * 2u, 0));
     r.beta = __builtin_amdgcn_raw_buffer_load_b16(beta, vb, unsigned(t0) * unsigned(ts_b) * 2u, 0);
   }
   __device__ __forceinline__ void qk(Raw& r, int t0) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      r.k[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(k, vk, (unsigned(t0) + i) * unsigned(ts_k) * 2u, 0));
-      r.q[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(q, vq, (unsigned(t0) + i) * unsigned(ts_q) * 2u, 0));
+      r.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(k, vk, (unsigned(t0) + i) * unsigned(ts_k) * 2u, 0));
+      r.q[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(q, vq, (unsigned(t0) + i) * unsigned(ts_q) * 2u, 0));
     }
   }
 };
-constexpr int kGateLoads = 5;  // vector memory operations of Loader::gate
-constexpr int kQkLoads = 8;    // ... of Loader::qk
 
-// Channel s (0..3) of a 4-channel bf16 group.
-__device__ __forceinline__ float chan4(uint2 w, int s) {
-  const uint32_t d = s < 2 ? w.x : w.y;
-  return (s & 1) ? bf16_hi(d) : bf16_lo(d);
-}
-
-// ---- producer: operands of one quarter ---------------------------------------------
+// ---- producer: operands of one half --------------------------------------------------
 // Writes 2^8 X, 2^8 Q, K' / 16 (package), 2^-8 K_G and (first half) bf16(K'^0
-// / 16) (scratch) of the quarter, its channels' Gam_h, and (channel half 0) b /
-// 16 and scale / |q| of the half's tokens.  The two channel halves of a half
-// exchange partial squared norms through NR (count nrm_ctr, target the
-// chunk's).  nvalid: tokens of the half inside the sequence (0..16).  The next
-// chunk's loads (token tn) are issued as soon as their registers are consumed;
-// `between` runs right after the gate loads are issued.
-template <int HF, int CH, typename Between>
-__device__ __forceinline__ void produce_quarter(Pack& P, Scratch& SC, Norms& NR, int* nrm_ctr,
-                                                int nrm_target, Raw& raw, const Loader& ld, int tn,
-                                                int nvalid, int lane, const float* c2, float c1,
-                                                float lb2, float scale, int* err, Between&& between) {
+// / 16) (scratch) of the half, Gam_h, b / 16 and scale / |q| of its tokens.
+// nvalid: tokens of the half inside the sequence (0..16).  The next loads
+// (token tn) are issued as soon as their registers are consumed.
+template <int HF>
+__device__ __forceinline__ void produce_half(Pack& P, Scratch& SC, Raw& raw, const Loader& ld, int tn,
+                                             int nvalid, int lane, const float (&c2)[8], float c1,
+                                             float lb2, float scale) {
   const int cg = lane & 15, tq = lane >> 4;
-  // partial squared norms of the lane's 4 tokens over this wave's 64 channels
-  float pk[4], pq[4];
+  // norms of the lane's 4 tokens (8 channels per lane, 16 lanes per row)
+  float rk[4], rq[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    pk[i] = row_sum(dot2(raw.k[i].y, dot2(raw.k[i].x, 0.f)));
-    pq[i] = row_sum(dot2(raw.q[i].y, dot2(raw.q[i].x, 0.f)));
+    const uint4 kk = raw.k[i], qq = raw.q[i];
+    rk[i] = __builtin_amdgcn_rsqf(row_sum(dot2(kk.w, dot2(kk.z, dot2(kk.y, dot2(kk.x, 0.f))))) + kNormEps);
+    rq[i] = __builtin_amdgcn_rsqf(row_sum(dot2(qq.w, dot2(qq.z, dot2(qq.y, dot2(qq.x, 0.f))))) + kNormEps) * scale;
   }
-  if (cg == 0) {
-    *reinterpret_cast<f32x4*>(&NR.kq[CH][4 * tq][0]) = f32x4{pk[0], pq[0], pk[1], pq[1]};
-    *reinterpret_cast<f32x4*>(&NR.kq[CH][4 * tq + 2][0]) = f32x4{pk[2], pq[2], pk[3], pq[3]};
-  }
-  arrive(nrm_ctr, lane);
   // gate sigma per (token, channel) and its running sum over the lane's 4
   // tokens; tokens past the sequence end get 1 / inf = 0
-  float cs[4][4];
+  float cs[8][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float pad = 4 * tq + i < nvalid ? 1.f : __builtin_inff();
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const float sg = rcp(ex2(fmaf(chan4(raw.g[i], s), c1, c2[s])) + pad);
+    for (int s = 0; s < 8; ++s) {
+      const float sg = rcp(ex2(fmaf(chan8(raw.g[i], s), c1, c2[s])) + pad);
       cs[s][i] = i == 0 ? sg : cs[s][i - 1] + sg;
     }
   }
   // beta / 16 of token cg of the half (lanes < 16), zero past the end
   const float bet = cg < nvalid ? rcp(1.f + ex2(-kLog2e * bf16_to_f32(uint16_t(raw.beta)))) * 0.0625f : 0.f;
   __builtin_amdgcn_sched_barrier(0);
-  ld.gate(raw, tn);  // next chunk's gate inputs and beta logit
+  ld.gate(raw, tn);  // next gate inputs and beta logit
   __builtin_amdgcn_sched_barrier(0);
-  between();
+  if (tq == 0) P.b16[kHT * HF + cg] = bet;
+  if (cg == 0) *reinterpret_cast<f32x4*>(&P.rqs[kHT * HF + 4 * tq]) = f32x4{rq[0], rq[1], rq[2], rq[3]};
   // earlier token groups' sums (rows of 16 lanes) and the half's total, per channel
-  float ex[4], tot[4], gam[4], ginv16[4];
+  float ex[8], tot[8];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < 8; ++s) {
     const unsigned t = __float_as_uint(cs[s][3]);
     const auto pr = __builtin_amdgcn_permlane16_swap(t, t, false, false);
     const float te = __uint_as_float(pr[0]), to = __uint_as_float(pr[1]);  // rows tq & ~1, tq | 1
@@ -452,49 +337,44 @@ __device__ __forceinline__ void produce_quarter(Pack& P, Scratch& SC, Norms& NR,
     const float p01 = __uint_as_float(pq2[0]), p23 = __uint_as_float(pq2[1]);
     ex[s] = ((tq & 2) ? p01 : 0.f) + ((tq & 1) ? te : 0.f);
     tot[s] = p01 + p23;
-    gam[s] = ex2(lb2 * tot[s]);
-    ginv16[s] = ex2(-lb2 * tot[s] - 4.f);  // Gam_h^-1 / 16
   }
-  // the other channel half's partial norms
-  wait_count(nrm_ctr, nrm_target, err);
-  const f32x4 o01 = *reinterpret_cast<const f32x4*>(&NR.kq[CH ^ 1][4 * tq][0]);
-  const f32x4 o23 = *reinterpret_cast<const f32x4*>(&NR.kq[CH ^ 1][4 * tq + 2][0]);
-  const float rk[4] = {__builtin_amdgcn_rsqf(pk[0] + o01[0] + kNormEps), __builtin_amdgcn_rsqf(pk[1] + o01[2] + kNormEps),
-                       __builtin_amdgcn_rsqf(pk[2] + o23[0] + kNormEps), __builtin_amdgcn_rsqf(pk[3] + o23[2] + kNormEps)};
-  if constexpr (CH == 0) {
-    if (tq == 0) P.b16[kHT * HF + cg] = bet;
-    if (cg == 0)
-      *reinterpret_cast<f32x4*>(&P.rqs[kHT * HF + 4 * tq]) =
-          f32x4{__builtin_amdgcn_rsqf(pq[0] + o01[1] + kNormEps) * scale, __builtin_amdgcn_rsqf(pq[1] + o01[3] + kNormEps) * scale,
-                __builtin_amdgcn_rsqf(pq[2] + o23[1] + kNormEps) * scale, __builtin_amdgcn_rsqf(pq[3] + o23[3] + kNormEps) * scale};
+  float ginv16[8];  // Gam_h^-1 / 16
+#pragma unroll
+  for (int s = 0; s < 8; ++s) ginv16[s] = ex2(-lb2 * tot[s] - 4.f);
+  if (tq == 0) {
+    float gam[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) gam[s] = ex2(lb2 * tot[s]);
+    *reinterpret_cast<f32x4*>(&P.gam[HF][gmo(8 * cg)]) = f32x4{gam[0], gam[1], gam[2], gam[3]};
+    *reinterpret_cast<f32x4*>(&P.gam[HF][gmo(8 * cg) + 4]) = f32x4{gam[4], gam[5], gam[6], gam[7]};
   }
-  if (tq == 0) *reinterpret_cast<f32x4*>(&P.gam[HF][gmo(64 * CH + 4 * cg)]) = f32x4{gam[0], gam[1], gam[2], gam[3]};
-  const int u16 = 8 * CH + (cg >> 1), hb = 4 * (cg & 1);                  // 16-byte unit, 8-byte half
-  const int kb = 2 * CH + (cg >> 3), hi = cg & 1, g = (cg >> 1) & 3;      // K' unit (kpo)
+  const int kb = cg >> 2, g = cg & 3;  // K' units (kpo): keys 8 cg + 4 hi .. + 3
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = kHT * HF + 4 * tq + i;
-    float vx[4], vq[4], vk[4], vg[4];
+    float vx[8], vq[8], vk[8], vg[8];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 8; ++s) {
       const float el = lb2 * ex[s];
       const float E = ex2(fmaf(cs[s][i], lb2, el + kShift));                   // 2^8 e^{G}
       const float Kq = ex2(fmaf(cs[s][i], -lb2, lb2 * tot[s] - el - 4.f));    // e^{G_last - G} / 16
-      const float kt = chan4(raw.k[i], s) * rk[i];
+      const float kt = chan8(raw.k[i], s) * rk[i];
       vx[s] = E * kt;
-      vq[s] = E * chan4(raw.q[i], s);
-      vk[s] = Kq * kt;                // K' / 16
-      vg[s] = vk[s] * ginv16[s];      // 2^-8 K_G
+      vq[s] = E * chan8(raw.q[i], s);
+      vk[s] = Kq * kt;                                        // K' / 16
+      vg[s] = vk[s] * ginv16[s];                              // 2^-8 K_G
     }
-    const int o = tro(t, u16) + hb;
-    *reinterpret_cast<uint2*>(&P.x[o]) = uint2{pkb(vx[0], vx[1]), pkb(vx[2], vx[3])};
-    *reinterpret_cast<uint2*>(&P.qt[o]) = uint2{pkb(vq[0], vq[1]), pkb(vq[2], vq[3])};
-    *reinterpret_cast<uint2*>(&SC.kg[o]) = uint2{pkb(vg[0], vg[1]), pkb(vg[2], vg[3])};
-    *reinterpret_cast<uint2*>(&P.kp[kpo(t, kb, hi, g)]) = uint2{pkh(vk[0], vk[1]), pkh(vk[2], vk[3])};
-    if constexpr (HF == 0) *reinterpret_cast<uint2*>(&SC.kp0[o]) = uint2{pkb(vk[0], vk[1]), pkb(vk[2], vk[3])};
+    const int o = tro(t, cg);
+    *reinterpret_cast<uint4*>(&P.x[o]) = uint4{pkb(vx[0], vx[1]), pkb(vx[2], vx[3]), pkb(vx[4], vx[5]), pkb(vx[6], vx[7])};
+    *reinterpret_cast<uint4*>(&P.qt[o]) = uint4{pkb(vq[0], vq[1]), pkb(vq[2], vq[3]), pkb(vq[4], vq[5]), pkb(vq[6], vq[7])};
+    *reinterpret_cast<uint4*>(&SC.kg[o]) = uint4{pkb(vg[0], vg[1]), pkb(vg[2], vg[3]), pkb(vg[4], vg[5]), pkb(vg[6], vg[7])};
+    *reinterpret_cast<uint2*>(&P.kp[kpo(t, kb, 0, g)]) = uint2{pkh(vk[0], vk[1]), pkh(vk[2], vk[3])};
+    *reinterpret_cast<uint2*>(&P.kp[kpo(t, kb, 1, g)]) = uint2{pkh(vk[4], vk[5]), pkh(vk[6], vk[7])};
+    if constexpr (HF == 0)
+      *reinterpret_cast<uint4*>(&SC.kp0[o]) = uint4{pkb(vk[0], vk[1]), pkb(vk[2], vk[3]), pkb(vk[4], vk[5]), pkb(vk[6], vk[7])};
   }
   __builtin_amdgcn_sched_barrier(0);
-  ld.qk(raw, tn);  // next chunk's q and k
+  ld.qk(raw, tn);  // next q and k
 }
 
 // ---- producer: products ---------------------------------------------------------------
@@ -663,164 +543,59 @@ __global__ __launch_bounds__(Cfg32<VS>::kThreads, 1) void fwd32_kernel(Params p)
   }
   __syncthreads();
 
-  const int bos = min(max(p.cu[n], 0), p.T);
-  const int eos = min(max(p.cu[n + 1], bos), p.T);
+  // the bounds are uniform: scalar registers (else every buffer access with a
+  // token offset in its scalar operand becomes a loop over lanes)
+  const int bos = __builtin_amdgcn_readfirstlane(min(max(p.cu[n], 0), p.T));
+  const int eos = __builtin_amdgcn_readfirstlane(min(max(p.cu[n + 1], bos), p.T));
   const int nc = (eos - bos + kC - 1) / kC;   // chunks
   int* err = &sm.sy.err;
 
-  // ---------------- producer waves: wave = 2 channel half + half ----------------
-  // Each chunk is built by all four producer waves, one quarter each (half HF
-  // of 16 tokens x channel half CH of 64); then two of them (rotating) form
-  // A and the inverse, and M.  Alone (no ring), the workgroup builds every
-  // chunk; with a ring, it builds the chunks of its slice's parity and
-  // copies the others from the partner workgroup's images.
-  auto producer = [&](auto hq, auto cq) {
-    constexpr int HF = decltype(hq)::value, CH = decltype(cq)::value, Q = 2 * CH + HF;
+  // ---------------- producer waves: wave = 2 slot + half ----------------
+  // Two producer slots of two waves each: slot k builds chunks k, k + 2, ..,
+  // wave (k, HF) the operands of half HF; then one of the two forms A and the
+  // inverse, the other M (alternating between chunks).
+  auto producer = [&](auto kq, auto hq) {
+    constexpr int K = decltype(kq)::value, HF = decltype(hq)::value;
     Loader ld;
     ld.q = rows_rsrc(p.q + size_t(h) * p.hs_q, eos, p.ts_q, kD);
     ld.k = rows_rsrc(p.k + size_t(h) * p.hs_k, eos, p.ts_k, kD);
     ld.g = rows_rsrc(p.g + size_t(h) * p.hs_g, eos, p.ts_g, kD);
     ld.beta = rows_rsrc(p.beta + size_t(h) * p.hs_b, eos, p.ts_b, 1);
     ld.ts_q = p.ts_q, ld.ts_k = p.ts_k, ld.ts_g = p.ts_g, ld.ts_b = p.ts_b;
-    ld.init(lane, 64 * CH);
+    ld.init(lane);
     const float eA = expf(p.A_log[h]);
     const float c1 = -kLog2e * eA;
     const float lb2 = p.lower_bound * kLog2e;
-    float c2[4];
+    float c2[8];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) c2[s] = c1 * p.dt_bias[h * kD + 64 * CH + 4 * (lane & 15) + s];
+    for (int s = 0; s < 8; ++s) c2[s] = c1 * p.dt_bias[h * kD + 8 * (lane & 15) + s];
     __builtin_amdgcn_sched_barrier(0);
     Raw raw;
-    // the products of a chunk: counter k picks the two waves (rotating)
-    auto products = [&](Pack& P, const Scratch& SC, int k, int* rdy) {
-      if (Q == (k & 3)) {
-        produce_inverse(P, SC, lane);
-        arrive_n(rdy, lane, 2);
-      } else if (Q == ((k + 2) & 3)) {
-        produce_m(P, SC, lane);
-        arrive_n(rdy, lane, 2);
-      }
-    };
-    // with a ring: share only with a partner on this XCD (its images are read
-    // through this XCD's L2); wave 0 finds out, the others wait for its word
-    bool share = false;
-    if (p.ring) {
-      int* ctl = p.ring_ctl + size_t(n * H + h) * kCtlInts;
-      if (Q == 0) {
-        int xcc;
-        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-        store_global(ctl + kCtlXcc + slice, (xcc & 15) + 1, lane);
-        poll_global(ctl + kCtlXcc + 1 - slice, 1, err);
-        const int other = sload_glc(ctl + kCtlXcc + 1 - slice);
-        if (lane == 0)
-          __hip_atomic_store(&sm.sy.mode, other == (xcc & 15) + 1 ? 1 : 2, __ATOMIC_RELEASE,
-                             __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-      wait_count(&sm.sy.mode, 1, err);
-      share = __builtin_amdgcn_readfirstlane(
-                  __hip_atomic_load(&sm.sy.mode, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) == 1;
-    }
-    if (!share) {
-      ld.gate(raw, bos + kHT * HF);
-      ld.qk(raw, bos + kHT * HF);
-      for (int j = 0; j < nc; ++j) {
-        const int c = j & 1, bf = (j >> 1) & 1;
-        Pack& P = sm.pk[c][bf];
-        Scratch& SC = sm.sc[c];
-        // the package buffer is free once every state wave is done with chunk j - 4,
-        // the scratch once the products of chunk j - 2 are
-        if (j >= 4) wait_row<NSW>(sm.sy.done[c], (j >> 1) - 1, err);
-        if (j >= 2) wait_count(&sm.sy.rdy[c][((j - 2) >> 1) & 1], 4 * (((j - 2) >> 2) + 1), err);
-        const int t0 = bos + kC * j + kHT * HF;
-        produce_quarter<HF, CH>(P, SC, sm.nr[c][HF], &sm.sy.nrm[c][HF], 2 * (j >> 1) + 2, raw, ld, t0 + kC,
-                                min(kHT, max(eos - t0, 0)), lane, c2, c1, lb2, p.scale, err, [] {});
-        arrive(&sm.sy.opnd[c], lane);
-        wait_count(&sm.sy.opnd[c], 4 * (j >> 1) + 4, err);
-        products(P, SC, j, &sm.sy.rdy[c][bf]);
-      }
-    } else {
-      const int s = slice;  // own chunks: 2 r + s
-      const int item = n * H + h;
-      int* ctl = p.ring_ctl + size_t(item) * kCtlInts;
-      const __amdgpu_buffer_rsrc_t ring = __builtin_amdgcn_make_buffer_rsrc(
-          p.ring + size_t(item) * (2 * kRing * kPackBytes), (short)0, 2 * kRing * kPackBytes, kRsrcWord3);
-      const int nr = (nc + 1) >> 1;
-      ld.gate(raw, bos + kC * s + kHT * HF);
-      ld.qk(raw, bos + kC * s + kHT * HF);
+    ld.gate(raw, bos + kC * K + kHT * HF);
+    ld.qk(raw, bos + kC * K + kHT * HF);
 #pragma unroll 1
-      for (int r = 0; r <= nr; ++r) {
-        const int j = 2 * r + s;              // own chunk of this round
-        const int jq = 2 * (r - 1) + 1 - s;   // the partner's chunk of the previous round
-        const int jo = 2 * (r - 1) + s;       // own chunk of the previous round
-        const bool own = r < nr && j < nc;
-        const bool rcv = r >= 1 && jq < nc;
-        // flag the previous own chunk's image (its stores are older than the
-        // gate loads just issued), then start copying the partner's
-        auto between = [&](auto after_gate) {
-          if (r >= 1 && jo < nc) {
-            if constexpr (decltype(after_gate)::value) vm_wait<kGateLoads>();
-            else vm_wait<0>();
-            store_global(ctl + s * 8 + ((r - 1) & 1) * 4 + Q, jo + 1, lane);
-          }
-          if (rcv) {
-            poll_global(ctl + (1 - s) * 8 + ((r - 1) & 1) * 4 + Q, jq + 1, err);
-            const int cq = jq & 1, bq = (jq >> 1) & 1;
-            if (jq >= 4) wait_row<NSW>(sm.sy.done[cq], (jq >> 1) - 1, err);
-            receive<Q>(sm.pk[cq][bq], ring, unsigned(((1 - s) * kRing + ((r - 1) & 1)) * kPackBytes), lane);
-          }
-        };
-        // the copy is in LDS: count it in
-        auto finish = [&]() { arrive(&sm.sy.rdy[jq & 1][(jq >> 1) & 1], lane); };
-        if (own) {
-          const int bf = r & 1;
-          Pack& P = sm.pk[s][bf];
-          Scratch& SC = sm.sc[s];
-          if (r >= 2) wait_row<NSW>(sm.sy.done[s], r - 1, err);
-          if (r >= 1) wait_count(&sm.sy.rdy[s][(r - 1) & 1], 4 * (((r - 1) >> 1) + 1), err);
-          const int t0 = bos + kC * j + kHT * HF;
-          produce_quarter<HF, CH>(P, SC, sm.nr[s][HF], &sm.sy.nrm[s][HF], 2 * r + 2, raw, ld, t0 + 2 * kC,
-                                  min(kHT, max(eos - t0, 0)), lane, c2, c1, lb2, p.scale, err,
-                                  [&] { between(std::integral_constant<bool, true>{}); });
-          arrive(&sm.sy.opnd[s], lane);
-          wait_count(&sm.sy.opnd[s], 4 * r + 4, err);
-          products(P, SC, r, &sm.sy.rdy[s][bf]);
-          // publish the complete package into ring slot r & 1 (free: the
-          // partner's flag seen in this round follows its copy of chunk j - 4)
-          wait_count(&sm.sy.rdy[s][bf], 4 * ((r >> 1) + 1), err);
-          publish<Q>(P, ring, unsigned((s * kRing + bf) * kPackBytes), lane);
-          if (rcv) {
-            vm_wait<kQkLoads + nblocks<Q>()>();  // the copy (older than the q/k loads and the stores)
-            finish();
-          }
-        } else {
-          between(std::integral_constant<bool, false>{});
-          if (rcv) {
-            vm_wait<0>();
-            finish();
-          }
-        }
-      }
-    }
-    vm_wait<0>();  // this wave's flag stores have reached the L2
-    arrive(&sm.sy.pdone, lane);
-    if (p.ring && Q == 0) {
-      // the second of the item's two workgroups to get here resets its words
-      // (every store of this workgroup is complete at the L2 before the count)
-      wait_count(&sm.sy.pdone, kProd, err);
-      vm_wait<0>();
-      if (lane == 0) {
-        int* ctl = p.ring_ctl + size_t(n * H + h) * kCtlInts;
-        if (__hip_atomic_fetch_add(ctl + kCtlDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 1) {
-          for (int w = 0; w < kCtlUsed; ++w) __hip_atomic_store(ctl + w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
+    for (int j = K; j < nc; j += 2) {
+      const int u = j >> 1, bf = u & 1;  // the slot's u-th chunk, package buffer bf
+      Pack& P = sm.pk[K][bf];
+      Scratch& SC = sm.sc[K];
+      // the package buffer is free once every state wave is done with chunk
+      // j - 4, the scratch once the products of chunk j - 2 are
+      if (j >= 4) wait_row<NSW>(sm.sy.done[K], u - 1, err);
+      if (j >= 2) wait_count(&sm.sy.rdy[K][bf ^ 1], 4 * (((u - 1) >> 1) + 1), err);
+      const int t0 = bos + kC * j + kHT * HF;
+      produce_half<HF>(P, SC, raw, ld, t0 + 2 * kC, min(kHT, max(eos - t0, 0)), lane, c2, c1, lb2, p.scale);
+      arrive(&sm.sy.opnd[K], lane);
+      wait_count(&sm.sy.opnd[K], 2 * (u + 1), err);
+      if (HF == (u & 1)) produce_inverse(P, SC, lane);
+      else produce_m(P, SC, lane);
+      arrive_n(&sm.sy.rdy[K][bf], lane, 2);
     }
   };
   if (wave < kProd) {
     switch (wave) {
       case 0: producer(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}); break;
-      case 1: producer(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}); break;
-      case 2: producer(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}); break;
+      case 1: producer(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}); break;
+      case 2: producer(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}); break;
       default: producer(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}); break;
     }
     if (lane == 0 && gave_up(err)) p.errword[0] = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -995,8 +770,7 @@ __global__ __launch_bounds__(Cfg32<VS>::kThreads, 1) void fwd32_kernel(Params p)
         ka[hb][rt] = tr4h(&P.kp[kpo(kHT * hb + 4 * g4 + (l16 >> 2), rt >> 1, rt & 1, l16 & 3)]);
     const float2 g1 = o.ga1;
     // done with chunk j's package (the K' reads above are complete before the
-    // count): said before waiting for chunk j + 1, which with a ring the
-    // producers may only copy in once they got a buffer back
+    // count), before waiting for chunk j + 1: the buffer goes back early
     arrive(&sm.sy.done[c][sw], lane);
     if (j + 1 < nc) {
       const int r1 = (j + 1) >> 1;

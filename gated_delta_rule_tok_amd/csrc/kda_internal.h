@@ -27,14 +27,8 @@ struct Params {
   const int32_t* cu;
   int32_t* order;  // sequence processing order (longest first), [N], in the workspace;
                    // null: the kernel ranks the sequences itself (pipelined kernels, N small)
-  int32_t* errword;  // the workspace's status word: a kernel sets it to 1 if a bounded
-                     // wait gave up (never cleared here)
-  // 32-token kernel with a value split of two: the two workgroups of a
-  // (sequence, head) share the chunk packages through these (null: each
-  // builds every chunk).  ring_ctl: kFwdCtlBytes per item, zero between calls;
-  // ring: kFwdRingBytes per item.  Items are sequence * H + head, < kFwdShareItems.
-  uint8_t* ring;
-  int32_t* ring_ctl;
+  int32_t* errword;  // the workspace's status word: a kernel sets it (nonzero) if a
+                     // bounded wait gave up (never cleared here)
   float lower_bound;
   float scale;
   // element strides of the per-token tensors (channels contiguous): row
@@ -120,8 +114,5 @@ hipError_t launch_pipe(const Params& p, hipStream_t stream);
 // columns, lower_bound in [-5.5, 0].  Ranks up to kInlineRankMax sequences
 // itself.
 hipError_t launch_fwd32(const Params& p, hipStream_t stream);
-constexpr int kFwdShareItems = 128;            // (sequence, head) items with a shared ring
-constexpr size_t kFwdCtlBytes = 256;           // control words per item
-constexpr size_t kFwdRingBytes = 4 * 30720;    // package images per item (2 slices x 2 slots)
 
 }  // namespace kda

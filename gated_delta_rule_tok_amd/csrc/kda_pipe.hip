@@ -66,7 +66,7 @@ constexpr int kTok = 16;  // tokens per chunk
 constexpr int kPW = 4;    // chunks per round
 constexpr int kPH = 2;    // producer waves per chunk (64-channel halves)
 constexpr int kProdWaves = kPW * kPH;
-constexpr int kSpinMax = 1 << 22;  // polls before a wait gives up (a safety bound, never reached)
+constexpr int kSpinMax = 1 << 22;  // polls before a wait gives up (then the status word is set)
 constexpr float kKpScale = 16.f;     // K' enters the fp16 state update times this
 constexpr float kNScale = 0.0625f;   // ... and N times this (exact inverse)
 
@@ -126,14 +126,21 @@ __device__ __forceinline__ void arrive(int* ctr, int lane) {
 }
 // Wait until *ctr >= target.  Every count a wave waits for is produced by
 // waves of the same workgroup that do not wait, directly or through others,
-// for the waiting wave, so the wait ends; the poll bound only keeps a broken
-// count from holding the device.
-__device__ __forceinline__ void wait_count(const int* ctr, int target) {
+// for the waiting wave, so the wait ends; the poll bound keeps a broken count
+// from holding the device, and giving up is recorded in the LDS word err
+// (every later wait then returns at once, so all waves finish quickly, and
+// the kernel reports it in the workspace's status word).
+__device__ __forceinline__ bool gave_up(const int* err) {
+  return __builtin_amdgcn_readfirstlane(__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != 0;
+}
+__device__ __forceinline__ void wait_count(const int* ctr, int target, int* err) {
+  if (gave_up(err)) return;
 #pragma unroll 1
   for (int it = 0; it < kSpinMax; ++it) {
-    if (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+    if (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
     __builtin_amdgcn_s_sleep(1);
   }
+  __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // One chunk's package: written by the chunk's two producer waves, read by
@@ -486,6 +493,7 @@ struct Sync {
   int done[kPW][4];
   int half[kPW];
   int rdy[2][kPW];
+  int err;  // a bounded wait gave up
 };
 
 // Wait until the first n counters of a 16-byte row are all >= target: one
@@ -494,7 +502,8 @@ struct Sync {
 // reads complete, the caller's writes are issued only after the exit branch
 // (which waits for the value), and the compiler barrier keeps them there.
 template <int n>
-__device__ __forceinline__ void wait_row(const int* row, int target) {
+__device__ __forceinline__ void wait_row(const int* row, int target, int* err) {
+  if (gave_up(err)) return;
 #pragma unroll 1
   for (int it = 0; it < kSpinMax; ++it) {
     typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -503,9 +512,13 @@ __device__ __forceinline__ void wait_row(const int* row, int target) {
     int m = d[0];
     if (n > 1) m = min(m, d[1]);
     if (n > 2) m = min(m, min(d[2], d[3]));
-    if (__builtin_amdgcn_readfirstlane(m) >= target) break;
+    if (__builtin_amdgcn_readfirstlane(m) >= target) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      return;
+    }
     __builtin_amdgcn_s_sleep(1);
   }
+  __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
@@ -567,8 +580,10 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   }
   __syncthreads();  // counters zeroed, ranking scratch read: the packages are free
 
-  const int bos = min(max(p.cu[n], 0), p.T);
-  const int eos = min(max(p.cu[n + 1], bos), p.T);
+  // the bounds are uniform: scalar registers (else every buffer access with a
+  // token offset in its scalar operand becomes a loop over lanes)
+  const int bos = __builtin_amdgcn_readfirstlane(min(max(p.cu[n], 0), p.T));
+  const int eos = __builtin_amdgcn_readfirstlane(min(max(p.cu[n + 1], bos), p.T));
   const int nc = (eos - bos + kTok - 1) / kTok;  // chunks
   const int nr = (nc + kPW - 1) / kPW;            // rounds
 
@@ -603,7 +618,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
       bf16* kg = sm.kg[r & 1][c];
       // the buffers are free once every state wave is done with round r - 2
       if (r >= 2)
-        wait_row<NSW>(sm.sy.done[c], r - 1);
+        wait_row<NSW>(sm.sy.done[c], r - 1, &sm.sy.err);
       const int t0 = bos + kTok * j, Lc = min(kTok, eos - t0);
       // this wave's next chunk (one round ahead) is loaded while the operands
       // are formed
@@ -614,7 +629,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
       produce_operands<false>(P, kg, raw, ld, tn, hf, Lc, lane, c2, c1, lb2, p.scale);
       // both halves' operands (the products run over all 128 channels)
       arrive(&sm.sy.half[c], lane);
-      wait_count(&sm.sy.half[c], kPH * (r + 1));
+      wait_count(&sm.sy.half[c], kPH * (r + 1), &sm.sy.err);
       if (hf == 0) produce_inverse(P, kg, lane);
       else produce_m(P, kg, lane);
       arrive(&sm.sy.rdy[r & 1][c], lane);
@@ -623,6 +638,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   if (wave < kProdWaves) {
     if (wave < kPW) producer(BufIdx<0>{});
     else producer(BufIdx<1>{});
+    if (lane == 0 && gave_up(&sm.sy.err)) p.errword[0] = 1;
     return;
   }
 
@@ -737,7 +753,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
       const int j = kPW * r + c;
       if (j >= nc) break;
       // both halves of the package: rounds B, B + 2, .., r on this buffer
-      wait_count(&sm.sy.rdy[B][c], kPH * ((r >> 1) + 1));
+      wait_count(&sm.sy.rdy[B][c], kPH * ((r >> 1) + 1), &sm.sy.err);
       const Pack& P = pk[B][c];
       const int t0 = bos + kTok * j;
 
@@ -842,6 +858,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   }
 
   store_state(p.sT, sbase);  // final state
+  if (lane == 0 && gave_up(&sm.sy.err)) p.errword[0] = 1;
 }
 
 }  // namespace

@@ -76,8 +76,10 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(Params p) {
   const float dtb0 = p.dt_bias[h * kD + 2 * lane];
   const float dtb1 = p.dt_bias[h * kD + 2 * lane + 1];
   // clamp the sequence to [0, T) so malformed offsets cannot leave the buffers
-  const int bos = min(max(p.cu[n], 0), p.T);
-  const int eos = min(max(p.cu[n + 1], bos), p.T);
+  // the bounds are uniform: scalar registers (else every buffer access with a
+  // token offset in its scalar operand becomes a loop over lanes)
+  const int bos = __builtin_amdgcn_readfirstlane(min(max(p.cu[n], 0), p.T));
+  const int eos = __builtin_amdgcn_readfirstlane(min(max(p.cu[n + 1], bos), p.T));
 
   for (int t0 = bos; t0 < eos; t0 += kTB) {
     const int nt = min(kTB, eos - t0);
@@ -222,8 +224,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p) {
   const float eA = expf(p.A_log[h]);
   const float dtb0 = p.dt_bias[h * kD + 2 * lane];
   const float dtb1 = p.dt_bias[h * kD + 2 * lane + 1];
-  const int bos = min(max(p.cu[n], 0), p.T);
-  const int eos = min(max(p.cu[n + 1], bos), p.T);
+  // the bounds are uniform: scalar registers (else every buffer access with a
+  // token offset in its scalar operand becomes a loop over lanes)
+  const int bos = __builtin_amdgcn_readfirstlane(min(max(p.cu[n], 0), p.T));
+  const int eos = __builtin_amdgcn_readfirstlane(min(max(p.cu[n + 1], bos), p.T));
 
   for (int t0 = bos; t0 < eos; t0 += kTB) {
     const int nt = min(kTB, eos - t0);

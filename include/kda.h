@@ -238,16 +238,6 @@ int kda_debug_set_vsplit(int s);
  */
 int kda_debug_set_kernel(int k);
 
-/*
- * Test hook: 0 (default): with a value split of two on the 32-token kernel,
- * the two workgroups of a (sequence, head) build alternate chunks' packages
- * and copy the other's through the workspace when the grid fits the device
- * at once; 1: never (each workgroup builds every chunk itself).  The results
- * are bit for bit the same either way.  Process-wide.  Returns the previous
- * setting, or -1 (unchanged) for an invalid value.
- */
-int kda_debug_set_share(int mode);
-
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,7 @@ def _write_counters(path, kernel, values_per_dispatch):
 
 def test_traffic_from_counters(tmp_path):
     pmc = str(tmp_path)
-    k = "void kda::(anonymous namespace)::fwd32_kernel<64, false>(kda::Params)"
+    k = "void kda::(anonymous namespace)::pipe_kernel<64>(kda::Params)"
     _write_counters(os.path.join(pmc, "fetch", "run_counter_collection.csv"), k,
                     [[600.0, 400.0], [500.0, 500.0]])          # 1000 KiB per dispatch
     _write_counters(os.path.join(pmc, "write", "run_counter_collection.csv"), k,

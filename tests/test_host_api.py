@@ -33,8 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == {"kda_get_workspace_size", "kda_chunk_prefill_fwd",
                           "kda_chunk_prefill_fwd_strided", "kda_chunk_prefill_fwd_checkpoints",
                           "kda_status_string",
-                          "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel",
-                          "kda_debug_set_share"}
+                          "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/kda.h but not exported"
 

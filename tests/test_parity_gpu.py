@@ -72,46 +72,29 @@ def test_vsplit_bit_identical(idx, kernel, splits):
 
 
 @pytest.mark.parametrize("case", ["config1", "config3", "ragged", "ranked"])
-def test_shared_packages_bit_identical(case):
-    """With a value split of two, the two workgroups of a (sequence, head)
-    build alternate chunks and copy the other's packages through the
-    workspace; the result is bit for bit that of each building every chunk,
-    and the status word stays clear."""
-    import torch
+def test_fwd32_kernel_parity(case):
+    """The 32-token kernel (the default for lower_bound < -5) matches the
+    oracle on the workloads and on ragged batches: lengths that end mid-chunk
+    and mid-half, one shorter than a chunk, an empty one, and more sequences
+    than the kernel ranks itself (the order table is built by a kernel
+    launched first)."""
     import gated_delta_rule_tok_amd as kda
     if case == "ragged":
-        # 8 (sequence, head) items, lengths that end mid-chunk and mid-half,
-        # one sequence shorter than a chunk and one empty
         x = KI.make_inputs([700, 33, 0, 1, 257, 64, 95, 16], 1, seed=41, init_state="fp32")
+        oref, fref = run_oracle(x)
     elif case == "ranked":
-        # 24 sequences x 5 heads = 120 items: the order table is built by a
-        # kernel launched first (more sequences than the kernel ranks itself),
-        # so the grid starts on whichever XCD the dispatcher is at
         lens = np.random.default_rng(43).integers(100, 600, 24).tolist()
         x = KI.make_inputs(lens, 5, seed=43, init_state="fp32")
-    else:
-        x, _ = _config(int(case[-1]))
-    d = to_device(x)
-    res = {}
-    prev_k = kda.kda_debug_set_kernel(5)
-    try:
-        kda.kda_debug_set_vsplit(2)
-        for mode in (1, 0, 0):
-            kda.kda_debug_set_share(mode)
-            o, f = run_gpu(x, d)
-            torch.cuda.synchronize()
-            res.setdefault(mode, []).append((o.view(torch.int16).cpu(), f.cpu()))
-    finally:
-        kda.kda_debug_set_share(0)
-        kda.kda_debug_set_kernel(prev_k)
-    solo = res[1][0]
-    for o, f in res[0]:
-        assert torch.equal(o, solo[0]), "out differs between shared and solo packages"
-        assert torch.equal(f, solo[1]), "final state differs between shared and solo packages"
-    if case in ("ragged", "ranked"):
         oref, fref = run_oracle(x)
-        assert_parity(x, res[0][0][0].view(torch.bfloat16).cuda(), res[0][0][1].cuda(), oref, fref,
-                      label=f"{case} shared")
+    else:
+        x, (oref, fref) = _config(int(case[-1]))
+    d = to_device(x)
+    prev = kda.kda_debug_set_kernel(5)
+    try:
+        out, fin = run_gpu(x, d)
+    finally:
+        kda.kda_debug_set_kernel(prev)
+    assert_parity(x, out, fin, oref, fref, label=f"32-token kernel {case}")
 
 
 @pytest.mark.parametrize("idx", [0, 1, 3])

@@ -15,7 +15,9 @@ in chunk order.  Three kinds of LDS counters order them:
 This test runs the same waits and counts as Python generators under random
 interleavings and checks that no wave reads a buffer that is incomplete or
 from another round, that no producer overwrites what a wave still reads, that
-the run always ends, and that planted off-by-one mistakes are caught.
+the run always ends, that planted off-by-one mistakes are caught, and that
+a wait which gives up (a bound on the number of polls) lets every wave finish
+with the error recorded.
 """
 from __future__ import annotations
 
@@ -30,8 +32,15 @@ class Violation(Exception):
     pass
 
 
-def run(nc: int, nsw: int, seed: int, bug: str | None = None) -> None:
-    """One random interleaving of the protocol for nc chunks and nsw state waves."""
+def run(nc: int, nsw: int, seed: int, bug: str | None = None, spin: int | None = None) -> int:
+    """One random interleaving of the protocol for nc chunks and nsw state waves;
+    returns the error flag (a wait gave up after spin polls)."""
+    st = {"err": 0}
+
+    def fail(msg):
+        # after a give-up the results are void: only the ending is checked
+        if not st["err"]:
+            raise Violation(msg)
     nr = (nc + KPW - 1) // KPW
     done = [[0] * 4 for _ in range(KPW)]
     half = [0] * KPW
@@ -44,7 +53,14 @@ def run(nc: int, nsw: int, seed: int, bug: str | None = None) -> None:
     kg_reading = {}  # (b, c) -> set of (half, round) reading kg now
 
     def wait(cond):
+        if st["err"]:
+            return
+        it = 0
         while not cond():
+            it += 1
+            if spin is not None and it > spin:
+                st["err"] = 1
+                return
             yield "blocked"
 
     def producer(c, hf):
@@ -59,12 +75,12 @@ def run(nc: int, nsw: int, seed: int, bug: str | None = None) -> None:
             # first phase: this half's operands of round r, and its kg part
             for s_r in reading.get((b, c), set()):
                 if s_r[1] != r:
-                    raise Violation(f"slot {c} buffer {b}: overwritten (round {r}) while wave {s_r[0]} reads round {s_r[1]}")
+                    fail(f"slot {c} buffer {b}: overwritten (round {r}) while wave {s_r[0]} reads round {s_r[1]}")
             pkg[(b, c, hf)] = (r, False)
             yield "run"
             for h_r in kg_reading.get((b, c), set()):
                 if h_r[1] != r:
-                    raise Violation(f"slot {c} buffer {b}: kg overwritten while half {h_r[0]} reads round {h_r[1]}")
+                    fail(f"slot {c} buffer {b}: kg overwritten while half {h_r[0]} reads round {h_r[1]}")
             kg[(b, c, hf)] = r
             yield "run"
             half[c] += 1
@@ -75,11 +91,11 @@ def run(nc: int, nsw: int, seed: int, bug: str | None = None) -> None:
             kg_reading.setdefault((b, c), set()).add((hf, r))
             for h in range(KPH):
                 if kg[(b, c, h)] != r:
-                    raise Violation(f"slot {c} buffer {b}: half {hf} reads kg of round {kg[(b, c, h)]} for round {r}")
+                    fail(f"slot {c} buffer {b}: half {hf} reads kg of round {kg[(b, c, h)]} for round {r}")
             yield "run"
             for h in range(KPH):
                 if kg[(b, c, h)] != r:
-                    raise Violation(f"slot {c} buffer {b}: kg changed under half {hf} in round {r}")
+                    fail(f"slot {c} buffer {b}: kg changed under half {hf} in round {r}")
             kg_reading[(b, c)].discard((hf, r))
             pkg[(b, c, hf)] = (r, True)
             yield "run"
@@ -98,11 +114,11 @@ def run(nc: int, nsw: int, seed: int, bug: str | None = None) -> None:
                 reading.setdefault((b, c), set()).add((s, r))
                 for hf in range(KPH):
                     if pkg[(b, c, hf)] != (r, True):
-                        raise Violation(f"wave {s} reads slot {c} buffer {b} for round {r}: half {hf} holds {pkg[(b, c, hf)]}")
+                        fail(f"wave {s} reads slot {c} buffer {b} for round {r}: half {hf} holds {pkg[(b, c, hf)]}")
                 yield "run"
                 for hf in range(KPH):
                     if pkg[(b, c, hf)] != (r, True):
-                        raise Violation(f"slot {c} buffer {b} changed under wave {s} in round {r}")
+                        fail(f"slot {c} buffer {b} changed under wave {s} in round {r}")
                 reading[(b, c)].discard((s, r))
                 done[c][s] += 1
                 yield "run"
@@ -114,18 +130,19 @@ def run(nc: int, nsw: int, seed: int, bug: str | None = None) -> None:
     while live:
         i = rng.choice(live)
         try:
-            st = next(waves[i])
+            ev = next(waves[i])
         except StopIteration:
             live.remove(i)
             blocked_rounds = 0
             continue
-        if st == "blocked":
+        if ev == "blocked":
             blocked_rounds += 1
             if blocked_rounds > 50 * len(live) + 1000:
                 # every live wave has been polled many times without progress
                 raise Violation("deadlock")
         else:
             blocked_rounds = 0
+    return st["err"]
 
 
 @pytest.mark.parametrize("nsw", [1, 2, 4])
@@ -144,3 +161,12 @@ def test_planted_mistakes_are_caught(bug):
         except Violation:
             caught += 1
     assert caught > 0, f"the model does not catch the planted mistake {bug}"
+
+
+def test_give_up_ends_every_wave():
+    """With a tiny poll bound some wait gives up: every wave still finishes
+    (later waits return at once) and the error is recorded."""
+    seen = 0
+    for seed in range(20):
+        seen += run(24, 4, seed, spin=2)
+    assert seen > 0
