@@ -16,6 +16,7 @@ kda_chunk_prefill_fwd_strided, with no copy.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 __all__ = ["kda_get_workspace_size", "kda_chunk_prefill_fwd", "kda_status_string",
@@ -104,8 +105,9 @@ def kda_get_workspace_size(max_tokens: int, heads: int, max_seqs: int) -> int:
 
 def kda_workspace_status(workspace) -> int:
     """The workspace's status word (its first 4 bytes, see include/kda.h): 0 while
-    every call that used it ran to completion normally; 1 once a kernel gave up
-    a bounded wait (the outputs of that call are void).  Synchronises the device."""
+    every call that used it ran to completion normally; nonzero (the kind of
+    wait, 1: LDS counters) once a kernel gave up a bounded wait (the outputs of
+    that call are void).  Synchronises the device."""
     import torch
     return int(workspace[:4].view(torch.int32)[0].item())
 
@@ -121,7 +123,7 @@ def kda_last_hip_error() -> str:
 def kda_debug_set_kernel(k: int) -> int:
     """Test hook: 0 automatic (default), 1 64-token kernel, 2 token-serial
     kernel, 3 token-serial kernel with decode staging, 4 pipelined 16-token
-    kernel (where it applies)."""
+    kernel (where it applies), 5 pipelined 32-token kernel."""
     prev = load_library().kda_debug_set_kernel(int(k))
     if prev < 0:
         raise ValueError(f"invalid kernel selector {k}")
@@ -155,6 +157,20 @@ def _check(t, name, dtype, shape=None, strided=False):
     elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous (dense row-major)")
     return t.data_ptr()
+
+
+def _flat(t, name, shape):
+    """t seen with `shape` without a copy: the library keeps only the data
+    pointer, and a temporary copy would go back to torch's allocator before
+    the queued kernel reads it."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (its data is read in place)")
+    if t.numel() != math.prod(shape):
+        raise ValueError(f"{name} has {t.numel()} elements, expected {math.prod(shape)}")
+    return t.view(shape)
 
 
 def kda_chunk_prefill_fwd(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound: float,
@@ -205,8 +221,8 @@ def kda_chunk_prefill_fwd(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound: 
         _check(q, "q", bf, (T, H, D), strided=True), _check(k, "k", bf, (T, H, D), strided=True),
         _check(v, "v", bf, (T, H, D), strided=True), _check(g, "g", bf, (T, H, D), strided=True),
         _check(beta_logits, "beta_logits", bf, (T, H), strided=True),
-        _check(A_log.reshape(-1), "A_log", torch.float32, (H,)),
-        _check(dt_bias.reshape(H, -1), "dt_bias", torch.float32, (H, D)),
+        _check(_flat(A_log, "A_log", (H,)), "A_log", torch.float32, (H,)),
+        _check(_flat(dt_bias, "dt_bias", (H, D)), "dt_bias", torch.float32, (H, D)),
     ]
     s0 = None if initial_state is None else _check(initial_state, "initial_state",
                                                    final_state.dtype, sshape)

@@ -109,10 +109,16 @@ namespace {
 
 // Stride checks of one [T, H, 128] tensor: non-negative multiples of 8
 // elements, and every row up to 256 past the end addressable with 32-bit
-// byte offsets.
+// byte offsets.  Each product and sum is checked for overflow (a caller's
+// stride near 2^63 must not wrap into range).
 bool rows_ok(int64_t ts, int64_t hs, int64_t T, int64_t H, int64_t rowlen, int64_t align) {
   if (ts < 0 || hs < 0 || ts % align || hs % align) return false;
-  return (T + 256) * ts + (H - 1) * hs + rowlen <= INT32_MAX;
+  if (ts > INT32_MAX || hs > INT32_MAX) return false;
+  int64_t rows = 0, heads = 0, end = 0;
+  if (__builtin_mul_overflow(T + 256, ts, &rows) || __builtin_mul_overflow(H - 1, hs, &heads) ||
+      __builtin_add_overflow(rows, heads, &end) || __builtin_add_overflow(end, rowlen, &end))
+    return false;
+  return end <= INT32_MAX;
 }
 
 kda_status_t forward(const void* q, const void* k, const void* v, const void* g,

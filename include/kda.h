@@ -24,7 +24,30 @@
  *
  * All device pointers are HIP device memory on the current device.  The caller
  * owns every buffer; the library allocates nothing and keeps no state between
- * calls except the test-only split override below.
+ * calls except the test-only overrides below.
+ *
+ * Status word.  The first 4 bytes of the workspace are an int32 status word.
+ * The caller zeroes it once before the workspace's first use (a zero-filled
+ * workspace is fine).  The pipelined kernels synchronise their waves through
+ * counters with a bounded number of polls; should a wait ever give up (a
+ * broken protocol, not an input condition), every wave finishes quickly and a
+ * kernel stores a nonzero kind in the status word (1: a wait on the
+ * workgroup's LDS counters): the outputs of that call are void.  The library
+ * never clears the word, so once the queued work has completed it reports
+ * every call made with the workspace since it was last zeroed.  Calls that
+ * may run concurrently need workspaces of their own (the sequence order table
+ * after the status word is rewritten by calls with more than 16 sequences).
+ *
+ * Numerics and input range.  Contractions take bf16 operands with fp32
+ * accumulation; the state stays fp32 between chunks.  The state update
+ * K'^T N takes fp16 operands, N / 16 where N is a chunk's corrected values
+ * (N = (I + A)^-1 diag(beta) (V - (e^G k) S)), so |N| must stay below
+ * 2^20: values v and state entries up to 2^14 in magnitude are supported
+ * (tested against the fp64 recurrence under relative bounds); N overflows to
+ * inf, and the state with it, only for inputs of order 2^18 and above.  Below
+ * the fp16 range's lower end, N / 16 keeps a relative precision of 2^-11
+ * down to 2^-14 and an absolute one of 2^-24 below, i.e. 2^-20 |K'| per term
+ * in the update.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -81,8 +104,10 @@ size_t kda_get_workspace_size(int64_t max_tokens, int32_t heads, int32_t max_seq
  *   final_state    [num_seqs, heads, 128, 128] in state_dtype (device); may be
  *                  the same pointer as initial_state (in-place update), any
  *                  other overlap is undefined
- *   workspace      device scratch of workspace_bytes bytes (may be NULL when
- *                  kda_get_workspace_size(...) is 0)
+ *   workspace      device memory of workspace_bytes bytes, at least
+ *                  kda_get_workspace_size(num_tokens, heads, num_seqs); its
+ *                  first 4 bytes are the status word (zero before the first
+ *                  call, see above)
  *   stream         hipStream_t to queue the work on (NULL = default stream)
  *
  * q, k, v, g, beta_logits and out may be NULL when num_tokens is 0; every other
@@ -182,16 +207,15 @@ kda_status_t kda_chunk_prefill_fwd_strided(
  *                        kda_chunk_prefill_fwd_strided.
  *
  * Every other argument, limit and guarantee is that of the forward call.
- * The work runs on the pipelined kernel whatever the call's size, so out and
- * final_state are bit for bit those of the forward call except for
- * decode-sized calls (at most 8 tokens per sequence on average), where the
- * forward call takes the token-serial decode kernel (both within the
- * tolerances of the oracle).  Returns
- * KDA_ERR_INVALID_ARG for a NULL checkpoints, a bad interval or a short
- * capacity, and KDA_ERR_UNSUPPORTED for lower_bound < -5 (that range is
- * served by the 64-token kernel, which writes no checkpoints) or under a
- * kda_debug_set_kernel / kda_debug_set_vsplit override that selects a kernel
- * other than the pipelined one.
+ * The work runs on a pipelined kernel whatever the call's size (the 16-token
+ * one for lower_bound >= -5, the 32-token one below), so out and final_state
+ * are bit for bit those of the forward call except for decode-sized calls (at
+ * most 8 tokens per sequence on average), where the forward call takes the
+ * token-serial decode kernel (both within the tolerances of the oracle).
+ * Returns KDA_ERR_INVALID_ARG for a NULL checkpoints, a bad interval or a
+ * short capacity, and KDA_ERR_UNSUPPORTED under a kda_debug_set_kernel /
+ * kda_debug_set_vsplit override that selects a kernel other than the
+ * pipelined ones.
  */
 kda_status_t kda_chunk_prefill_fwd_checkpoints(
     const void* q, const void* k, const void* v, const void* g, const void* beta_logits,
@@ -223,18 +247,25 @@ const char* kda_last_hip_error(void);
 int kda_debug_set_vsplit(int s);
 
 /*
- * Test hook: choose the kernel family -- 0 (default): automatic: calls with
- * at most 8 tokens per sequence on average (decode-sized) take the
- * token-serial kernel with 4-token staging; otherwise the pipelined 16-token
- * chunk kernel for lower_bound >= -5 with the value dimension split at least
- * in two, else the 64-token kernel.  1: the 64-token chunk kernel (WY/UT with
- * a blocked forward substitution over the 64x64 triangle); 2: the
- * token-serial fp32 kernel (32-token staging), an independent GPU
- * implementation of the same recurrence used to cross-check the chunked ones;
- * 3: the token-serial kernel with 4-token staging; 4: the pipelined kernel
- * whatever the call's size (falling back as in 0 where it does not apply).
- * Process-wide.  Returns the previous setting, or -1 (unchanged) for an
- * invalid value.
+ * Test hook: choose the kernel family -- 0 (default): automatic.  A call
+ * with at most 8 tokens per sequence on average over the whole batch
+ * (num_tokens <= 8 * num_seqs: decode-sized) takes the token-serial kernel
+ * with 4-token staging, whatever its longest sequence; any other call the
+ * pipelined 16-token chunk kernel for lower_bound >= -5, else the pipelined
+ * 32-token kernel, both with the value dimension split at least in two.  The
+ * choice is by the batch's average, so one sequence's result may come from
+ * either kernel depending on what it is batched with: both follow the
+ * recurrence within the tolerances of the oracle, but they are not bit for
+ * bit the same.  1: the 64-token chunk kernel (WY/UT with a blocked forward
+ * substitution over the 64x64 triangle); 2: the token-serial fp32 kernel
+ * (32-token staging), an independent GPU implementation of the same
+ * recurrence used to cross-check the chunked ones; 3: the token-serial kernel
+ * with 4-token staging; 4: the pipelined 16-token kernel whatever the call's
+ * size (lower_bound < -5 goes to the 32-token kernel, a forced unsplit launch
+ * to the 64-token kernel); 5: the pipelined 32-token kernel (chunks of two
+ * 16-token halves, each with its own decay reference) whatever the call's
+ * size.  Process-wide.  Returns the previous setting, or -1 (unchanged) for
+ * an invalid value.
  */
 int kda_debug_set_kernel(int k);
 

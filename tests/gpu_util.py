@@ -103,14 +103,26 @@ def to_f64(t) -> np.ndarray:
 
 def diff_stats(gpu: np.ndarray, ref: np.ndarray) -> dict:
     if gpu.size == 0:
-        return dict(max_abs=0.0, mean_abs=0.0, rel_rms=0.0)
+        return dict(max_abs=0.0, mean_abs=0.0, rel_rms=0.0, ref_max=0.0, ref_mean=0.0)
     d = np.abs(gpu - ref)
+    a = np.abs(ref)
     return dict(max_abs=float(d.max()), mean_abs=float(d.mean()),
-                rel_rms=float(np.sqrt((d * d).sum() / max((ref * ref).sum(), 1e-300))))
+                rel_rms=float(np.sqrt((d * d).sum() / max((ref * ref).sum(), 1e-300))),
+                ref_max=float(a.max()), ref_mean=float(a.mean()))
 
 
-# Relative bounds for inputs whose state grows far beyond the workloads' scale
-# (weak or no decay): bf16 operands give ~2^-9 relative error per product.
+# Relative bounds for inputs far from the workloads' scale (weak or no decay,
+# where the state keeps growing; values of large magnitude).  A bf16 rounding
+# adds about 2^-9 / sqrt(3) = 1.1e-3 relative RMS error; an output carries
+# three or four of them (its product's two operands and its own rounding),
+# about 2-2.5e-3 in all, the fp32 state fewer.  The mean error relative to the
+# mean magnitude is of the same size as the RMS ratio.  The bounds leave about
+# 2x room:
+#   max|d|  <= REL_MAX  * max|ref|
+#   mean|d| <= REL_MEAN * mean|ref|
+#   RMS(d)  <= REL_RMS  * RMS(ref)
+REL_MAX = 1e-2
+REL_MEAN = 5e-3
 REL_RMS_OUT = 5e-3
 REL_RMS_STATE = 3e-3
 
@@ -118,8 +130,9 @@ REL_RMS_STATE = 3e-3
 def assert_parity(x: KI.KdaInputs, out_gpu, fin_gpu, out_ref, fin_ref, label="", rows=None,
                   relative=False):
     """max|d| and mean|d| bounds on out (rows of tokens inside sequences) and on
-    the final state.  relative=True keeps the max|d| bound and replaces the
-    absolute mean|d| bound by relative-RMS bounds."""
+    the final state.  relative=True scales every bound by the reference's own
+    magnitude (REL_MAX, REL_MEAN, REL_RMS_*; the absolute max bound still
+    holds where it is the looser one)."""
     tol = MAX_ABS_BF16_STATE if x.state_bf16 else MAX_ABS_FP32_STATE
     if rows is None:
         rows = np.concatenate([np.arange(x.cu_seqlens[i], x.cu_seqlens[i + 1])
@@ -128,8 +141,10 @@ def assert_parity(x: KI.KdaInputs, out_gpu, fin_gpu, out_ref, fin_ref, label="",
     sf = diff_stats(to_f64(fin_gpu), fin_ref)
     print(f"[parity] {label} out {so} final {sf}", flush=True)
     if relative:
-        assert so["max_abs"] <= tol and so["rel_rms"] <= REL_RMS_OUT, f"{label} out: {so}"
-        assert sf["max_abs"] <= tol and sf["rel_rms"] <= REL_RMS_STATE, f"{label} final: {sf}"
+        for st, rms, what in ((so, REL_RMS_OUT, "out"), (sf, REL_RMS_STATE, "final state")):
+            assert st["max_abs"] <= max(tol, REL_MAX * st["ref_max"]), f"{label} {what}: {st}"
+            assert st["mean_abs"] <= REL_MEAN * st["ref_mean"] + 1e-12, f"{label} {what}: {st}"
+            assert st["rel_rms"] <= rms, f"{label} {what}: {st}"
         return so, sf
     assert so["max_abs"] <= tol and so["mean_abs"] <= MEAN_ABS, f"{label} out: {so}"
     assert sf["max_abs"] <= tol and sf["mean_abs"] <= MEAN_ABS, f"{label} final state: {sf}"

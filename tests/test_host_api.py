@@ -185,6 +185,12 @@ def test_strided_entry_checks():
     assert _call_strided(st, T=16384) == INVALID
     st.q_token = 16 * 128 * 4
     assert _call_strided(st, T=16384, lb=-7.0) == UNSUPPORTED  # strides accepted
+    # strides whose products would wrap a 64-bit integer are rejected, not wrapped
+    for field in ("q_token", "k_head", "g_token", "beta_head"):
+        for value in (2 ** 55, 2 ** 62, 2 ** 63 - 8):
+            st = _dense_strides(16)
+            setattr(st, field, value)
+            assert _call_strided(st) == INVALID, (field, value)
 
 
 def test_python_binding_strided_views_keep_channel_contiguity():
@@ -195,6 +201,25 @@ def test_python_binding_strided_views_keep_channel_contiguity():
     with pytest.raises((ValueError, TypeError)):
         # channels not contiguous (stride 2): rejected before anything else
         kda._check(big[..., ::2], "q", bf, (T, H, 128), strided=True)
+
+
+def test_python_binding_never_copies_parameters():
+    """A_log and dt_bias are passed by data pointer: a non-contiguous tensor
+    is rejected instead of copied into a temporary that torch could recycle
+    before the queued kernel reads it."""
+    torch = pytest.importorskip("torch")
+    H = 4
+    a = torch.zeros(2 * H)
+    with pytest.raises(ValueError):
+        kda._flat(a[::2], "A_log", (H,))
+    d = torch.zeros(128, H).t()
+    with pytest.raises(ValueError):
+        kda._flat(d, "dt_bias", (H, 128))
+    with pytest.raises(ValueError):
+        kda._flat(torch.zeros(H + 1), "A_log", (H,))
+    flat = torch.zeros(H, 1)
+    v = kda._flat(flat, "A_log", (H,))
+    assert v.data_ptr() == flat.data_ptr() and tuple(v.shape) == (H,)
 
 
 def test_debug_kernel_hook():

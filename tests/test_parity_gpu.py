@@ -211,8 +211,8 @@ def test_saturated_gate(lb):
 @pytest.mark.parametrize("lb", [0.0, -0.05])
 def test_weak_or_no_decay(lb):
     """Without decay the state keeps growing (|S| ~8x the workloads' scale at
-    216 tokens), so the absolute mean bound calibrated on the workloads does not
-    apply; the max bound does, and the error stays at bf16 relative precision."""
+    216 tokens), so the bounds calibrated on the workloads do not apply; every
+    bound is scaled by the reference's magnitude (max, mean and RMS)."""
     x = KI.make_inputs([150, 66], 2, seed=35, init_state="fp32", lower_bound=lb)
     d = to_device(x)
     out, fin = run_gpu(x, d)
@@ -312,3 +312,72 @@ def test_decode_sized_calls(lengths, state, lb):
         finally:
             kda.kda_debug_set_kernel(prev)
         assert_parity(x, out, fin, oref, fref, label=f"decode-sized kernel {kernel}")
+
+
+def _bf16_bits(vals):
+    return KI.f32_to_bf16_bits(np.asarray(vals, np.float32))
+
+
+def _degenerate_inputs():
+    """A ragged batch with the method's degenerate rows: all-zero q rows, all-zero
+    k rows (normalised to zero: the eps under the root keeps them finite), beta
+    logits of +inf and -inf (beta exactly 1 and 0) and gate inputs of +-256
+    (the sigmoid saturated: decay exactly e^lower_bound or none)."""
+    x = KI.make_inputs([150, 1, 47, 0, 96, 33], 3, seed=51, init_state="fp32")
+    rng = np.random.default_rng(52)
+    T = x.T
+    zq = rng.choice(T, 20, replace=False)
+    zk = rng.choice(T, 20, replace=False)
+    x.q[zq] = 0
+    x.k[zk] = 0
+    x.k[zq[:3]] = 0                       # some rows with both q and k zero
+    binf = rng.choice(T, 30, replace=False)
+    x.beta_logits[binf[:15], 0] = _bf16_bits(np.inf)
+    x.beta_logits[binf[15:], 1] = _bf16_bits(-np.inf)
+    x.beta_logits[binf[:5], 2] = _bf16_bits(-np.inf)
+    gt = rng.choice(T, 40, replace=False)
+    x.g[gt[:20], :, :64] = _bf16_bits(256.0)
+    x.g[gt[20:], :, 64:] = _bf16_bits(-256.0)
+    x.g[gt[:10], 1, :] = _bf16_bits(-256.0)
+    return x
+
+
+@pytest.mark.parametrize("kernel", [0, 4, 5, 1, 2, 3])
+def test_degenerate_rows(kernel):
+    """Zero q / k rows, infinite beta logits and saturated gates, on every
+    kernel family, against the oracle."""
+    import gated_delta_rule_tok_amd as kda
+    x = _degenerate_inputs()
+    print(f"[case] degenerate rows kernel={kernel} T={x.T} H={x.H}", flush=True)
+    d = to_device(x)
+    oref, fref = run_oracle(x)
+    assert np.isfinite(oref).all() and np.isfinite(fref).all()
+    prev = kda.kda_debug_set_kernel(kernel)
+    try:
+        out, fin = run_gpu(x, d)
+    finally:
+        kda.kda_debug_set_kernel(prev)
+    assert_parity(x, out, fin, oref, fref, label=f"degenerate rows kernel {kernel}")
+
+
+@pytest.mark.parametrize("kernel", [0, 5])
+@pytest.mark.parametrize("log2_scale", [10, 12, 14])
+def test_large_values(log2_scale, kernel):
+    """Values and initial state of magnitude 2^10 .. 2^14 (the range the
+    header states for the fp16 state update): every bound relative to the
+    reference's magnitude."""
+    import gated_delta_rule_tok_amd as kda
+    x = KI.make_inputs([150, 66, 200], 2, seed=53, init_state="fp32")
+    f = np.float32(2.0 ** log2_scale)
+    x.v[:] = KI.f32_to_bf16_bits(KI.bf16_bits_to_f32(x.v) * f)
+    x.initial_state[:] = x.initial_state * (f / np.float32(0.02 * 4))
+    print(f"[case] large values 2^{log2_scale} kernel={kernel}", flush=True)
+    d = to_device(x)
+    oref, fref = run_oracle(x)
+    prev = kda.kda_debug_set_kernel(kernel)
+    try:
+        out, fin = run_gpu(x, d)
+    finally:
+        kda.kda_debug_set_kernel(prev)
+    assert_parity(x, out, fin, oref, fref, label=f"|v| ~ 2^{log2_scale} kernel {kernel}",
+                  relative=True)

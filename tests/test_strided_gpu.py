@@ -2,10 +2,10 @@
 through the binding) give the dense call's results bit for bit, on every kernel
 family, and leave the rest of the output buffer untouched.
 
-The strided entry point is the SURVEY "next" row f1: the pages' wrapper
-listing (vLLM PR #55737's report, "Key source snippets") copies q, k, v, g to
-dense tensors because FlashKDA fixes their strides, and its "Risks" list counts
-the cost of those copies.
+The pages' wrapper listing (vLLM PR #55737's report, "Key source snippets")
+copies q, k, v, g to dense tensors because FlashKDA fixes their strides, and
+its "Risks" list counts the cost of those copies; the strided entry point
+takes the views as they are.
 
 PYTEST_DONT_REWRITE: failing asserts must not repr device tensors.
 """
@@ -47,7 +47,7 @@ def _strided_views(d, layout):
     return sd, out, obuf
 
 
-@pytest.mark.parametrize("kernel", [4, 1, 2, 3])
+@pytest.mark.parametrize("kernel", [4, 5, 1, 2, 3])
 @pytest.mark.parametrize("layout", ["fused_rows", "per_head"])
 def test_strided_matches_dense_bitwise(kernel, layout):
     import torch
@@ -71,7 +71,7 @@ def test_strided_matches_dense_bitwise(kernel, layout):
 
 
 def test_strided_parity_bf16_state_strong_bound():
-    """Strided views on the bf16-state path with lower_bound -5.5 (the 64-token
+    """Strided views on the bf16-state path with lower_bound -5.5 (the 32-token
     kernel), against the oracle."""
     import torch
     x = KI.make_inputs([200, 31], 2, seed=42, init_state="bf16", lower_bound=-5.5)
@@ -82,3 +82,23 @@ def test_strided_parity_bf16_state_strong_bound():
     torch.cuda.synchronize()
     oref, fref = run_oracle(x)
     assert_parity(x, out_s, fin_s, oref, fref, label="strided bf16 state lb=-5.5")
+
+
+def test_strided_headline_workload_matches_oracle():
+    """The 8 x 2048, H = 16 workload as a caller holding a fused projection
+    output would pass it: q, k, v, g as views into one [T, 4 H 128] buffer,
+    beta a strided column slice, out the second half of a wider buffer; the
+    default kernel choice, every element against the oracle, and the first
+    half of the output buffer untouched."""
+    import torch
+    x = KI.config_inputs(1)
+    print(f"[case] strided headline T={x.T} H={x.H} N={x.N}", flush=True)
+    d = to_device(x)
+    sd, out_s, obuf = _strided_views(d, "fused_rows")
+    _, fin_s, ws = alloc_outputs(x, d)
+    run_gpu(x, sd, out=out_s, fin=fin_s, ws=ws)
+    torch.cuda.synchronize()
+    oref, fref = run_oracle(x)
+    assert_parity(x, out_s, fin_s, oref, fref, label="strided 8x2048 H=16")
+    untouched = obuf[..., :128].view(torch.int16)
+    assert bool((untouched == SENTINEL).all()), "strided out wrote outside its rows"
