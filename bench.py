@@ -58,11 +58,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-KERNEL = "pipe_kernel"  # the dominant kernel of a call (the 16-token pipelined forward)
+def dominant_kernel(decode: bool, lower_bound: float) -> str:
+    """The kernel a call's time goes to (the library's automatic choice):
+    the token-serial decode kernel for decode-sized calls, else the 16-token
+    pipelined kernel for lower_bound >= -5 and the 32-token one below."""
+    if decode:
+        return "decode_kernel"
+    return "pipe_kernel" if lower_bound >= -5.0 else "fwd32_kernel"
 
 
-def traffic_file(workload: str) -> str:
-    return os.path.join(PROFILES, f"traffic__{KERNEL}__{workload}.json")
+def traffic_file(workload: str, kernel: str) -> str:
+    return os.path.join(PROFILES, f"traffic__{kernel}__{workload}.json")
 
 
 def _pmc_sum(path: str, kernel_sub: str):
@@ -76,19 +82,19 @@ def _pmc_sum(path: str, kernel_sub: str):
     return (sum(per.values()) / len(per), len(per)) if per else (None, 0)
 
 
-def traffic_from_pmc(pmc_dir: str, workload: str, command: str) -> dict:
+def traffic_from_pmc(pmc_dir: str, workload: str, command: str, kernel: str) -> dict:
     """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) of the
     benchmark and of a plain device copy of known size into HBM bytes per
     launch of the dominant kernel.  Expects pmc_dir/{fetch,write,cal_fetch,cal_write}/
     run_counter_collection.csv; the calibration copy moves 256 MiB."""
     f = lambda d: os.path.join(pmc_dir, d, "run_counter_collection.csv")
-    fetch, nf = _pmc_sum(f("fetch"), KERNEL)
-    write, nw = _pmc_sum(f("write"), KERNEL)
+    fetch, nf = _pmc_sum(f("fetch"), kernel)
+    write, nw = _pmc_sum(f("write"), kernel)
     cal_f, _ = _pmc_sum(f("cal_fetch"), "copyBuffer")
     cal_w, _ = _pmc_sum(f("cal_write"), "copyBuffer")
     copy_kib = 256 * 1024
     fs, ws = copy_kib / cal_f, copy_kib / cal_w
-    out = {"kernel_source_sha256": kernel_source_hash(), "workload": workload,
+    out = {"kernel_source_sha256": kernel_source_hash(), "workload": workload, "kernel": kernel,
            "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
            "dispatches": [nf, nw], "fetch_scale": fs, "write_scale": ws,
            "calibration": "device copy of 256 MiB: FETCH_SIZE %.0f KiB, WRITE_SIZE %.0f KiB"
@@ -97,6 +103,22 @@ def traffic_from_pmc(pmc_dir: str, workload: str, command: str) -> dict:
            "read_bytes": fetch * fs * 1024.0, "write_bytes": write * ws * 1024.0,
            "command": command}
     return out
+
+
+def workload_name(args):
+    """(workload name, dominant kernel, the selecting arguments) of a run."""
+    import kda_inputs as KI
+    if args.decode_batch:
+        wl, lb = f"decode_{args.decode_batch}x1_h16", KI.LOWER_BOUND
+        sel = f"--decode-batch {args.decode_batch}"
+    else:
+        wl, lb = KI.CONFIGS[args.config]["name"], KI.LOWER_BOUND
+        sel = f"--config {args.config}"
+    if args.lower_bound is not None:
+        lb = float(args.lower_bound)
+        wl += f"_lb{args.lower_bound:g}"
+        sel += f" --lower-bound {args.lower_bound:g}"
+    return wl, dominant_kernel(bool(args.decode_batch), lb), sel
 
 
 def main():
@@ -111,6 +133,12 @@ def main():
     ap.add_argument("--checkpoint-interval", type=int, default=0,
                     help="also write the state every this many tokens of each sequence "
                          "(kda_chunk_prefill_fwd_checkpoints); 0: off")
+    ap.add_argument("--lower-bound", type=float, default=None,
+                    help="override the workload's lower_bound (below -5 the 32-token kernel runs; "
+                         "not the headline configuration)")
+    ap.add_argument("--decode-batch", type=int, default=0,
+                    help="instead of --config: this many one-token sequences, 16 heads, fp32 "
+                         "state (a decode step; the token-serial decode kernel runs)")
     ap.add_argument("--settle-ms", type=float, default=200.0,
                     help="run the call this long before the warmup steps (clock ramp; 0: none)")
     ap.add_argument("--traffic-from", metavar="PMC_DIR",
@@ -131,17 +159,16 @@ def main():
         return
 
     if args.traffic_from:
-        import kda_inputs as KI
-        wl = KI.CONFIGS[args.config]["name"]
+        wl, kernel, sel = workload_name(args)
         cmd = ("cd /tmp && export TMPDIR=/tmp; for c in FETCH_SIZE WRITE_SIZE: rocprofv3 --pmc $c "
-               "--output-format csv -d <pmc>/<fetch|write> -o run -- python bench.py --config "
-               f"{args.config} --steps 3 --warmup 1 --settle-ms 0 --no-cpu --no-graph; "
+               f"--output-format csv -d <pmc>/<fetch|write> -o run -- python bench.py {sel} "
+               "--steps 3 --warmup 1 --settle-ms 0 --no-cpu --no-graph; "
                "rocprofv3 --pmc $c --output-format csv "
                "-d <pmc>/<cal_fetch|cal_write> -o run -- python bench.py --copy-calibration; "
-               f"python bench.py --config {args.config} --traffic-from <pmc>")
-        t = traffic_from_pmc(args.traffic_from, wl, cmd)
+               f"python bench.py {sel} --traffic-from <pmc>")
+        t = traffic_from_pmc(args.traffic_from, wl, cmd, kernel)
         os.makedirs(PROFILES, exist_ok=True)
-        with open(traffic_file(wl), "w") as fh:
+        with open(traffic_file(wl, kernel), "w") as fh:
             json.dump(t, fh, indent=1)
         print(json.dumps(t))
         return
@@ -157,7 +184,13 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    x = KI.config_inputs(args.config)
+    if args.decode_batch:
+        x = KI.make_inputs([1] * args.decode_batch, 16, seed=7, init_state="fp32")
+    else:
+        x = KI.config_inputs(args.config)
+    if args.lower_bound is not None:
+        x.lower_bound = float(args.lower_bound)
+    x.meta["config"], kernel, _ = workload_name(args)
     T, H, N = x.T, x.H, x.N
     sbytes = 2 if x.state_bf16 else 4
     sdtype = torch.bfloat16 if x.state_bf16 else torch.float32
@@ -287,7 +320,7 @@ def main():
     achieved_gbs = abytes / (launch_ms * 1e-3) / 1e9
 
     traffic = None
-    tf = traffic_file(x.meta["config"])
+    tf = traffic_file(x.meta["config"], kernel)
     if os.path.exists(tf) and not args.checkpoint_interval:  # counters of the plain call
         t = json.load(open(tf))
         if t.get("kernel_source_sha256") == kernel_source_hash():
@@ -317,7 +350,7 @@ def main():
                    "initial_state": x.initial_state is not None, "buffer_sets": len(sets),
                    **({"checkpoint_interval": args.checkpoint_interval, "checkpoints": n_ck}
                       if args.checkpoint_interval else {})},
-        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": abytes, "launch_us": launch_ms * 1e3,
                      "measured_copy_GBps": copy_gbs,
@@ -326,7 +359,11 @@ def main():
 
     if not args.no_cpu:
         import oracle
-        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        # the oracle parallelises over (sequence, head) items: as many threads
+        # as it has items, at most the CPUs this process may run on
+        host_cpus = os.cpu_count()
+        affinity = len(os.sched_getaffinity(0))
+        threads = max(1, min(affinity, N * H))
         # whole-workload passes, repeated until about 3 s of wall clock (at most
         # 7 passes); the median pass is reported
         times = []
@@ -339,6 +376,7 @@ def main():
         cpu_s = float(np.median(times))
         result["cpu_baseline"] = {
             "value": T / cpu_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host_cpu_count": host_cpus, "affinity_cpus": affinity, "threads_used": threads,
             "sample": f"the whole {x.meta['config']} workload ({T} tokens x {H} heads), "
                       f"fp64 token recurrence, {threads} threads over (sequence, head); "
                       f"median of {len(times)} passes, {cpu_s:.2f} s each"}

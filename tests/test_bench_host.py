@@ -42,9 +42,17 @@ def test_traffic_from_counters(tmp_path):
                     "__amd_rocclr_copyBuffer", [[128 * 1024.0]])
     _write_counters(os.path.join(pmc, "cal_write", "run_counter_collection.csv"),
                     "__amd_rocclr_copyBuffer", [[256 * 1024.0]])
-    t = bench.traffic_from_pmc(pmc, "w", "cmd")
+    t = bench.traffic_from_pmc(pmc, "w", "cmd", "pipe_kernel")
     assert t["fetch_kib_per_dispatch"] == 1000.0 and t["write_kib_per_dispatch"] == 500.0
     assert t["dispatches"] == [2, 1]
     assert t["fetch_scale"] == 2.0 and t["write_scale"] == 1.0
     assert t["bytes_per_launch"] == (1000.0 * 2.0 + 500.0) * 1024.0
     assert t["kernel_source_sha256"] == bench.kernel_source_hash()
+
+
+def test_dominant_kernel_follows_the_library_choice():
+    import bench
+    assert bench.dominant_kernel(True, -5.0) == "decode_kernel"
+    assert bench.dominant_kernel(False, -5.0) == "pipe_kernel"
+    assert bench.dominant_kernel(False, -1.0) == "pipe_kernel"
+    assert bench.dominant_kernel(False, -5.25) == "fwd32_kernel"
