@@ -21,7 +21,7 @@ import os
 
 __all__ = ["kda_get_workspace_size", "kda_chunk_prefill_fwd", "kda_status_string",
            "kda_workspace_status",
-           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel", "KdaError", "library_path", "load_library"]
+           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel", "kda_spec_decode_step", "KdaError", "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -87,6 +87,9 @@ def load_library():
             P, P, P, P, P, P, P, F, F, P, P, P, P, P, P, I64, I32, I32, ctypes.c_int, SZ,
             ctypes.POINTER(_Strides), P, I32, I64]
         lib.kda_chunk_prefill_fwd_checkpoints.restype = ctypes.c_int
+        lib.kda_spec_decode_step.argtypes = [P, P, P, P, P, P, P, F, F, P, I64, P, P, I32, P, P,
+                                             P, P, I64, I32, I32, ctypes.c_int, SZ]
+        lib.kda_spec_decode_step.restype = ctypes.c_int
         lib.kda_status_string.argtypes = [ctypes.c_int]
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_last_hip_error.argtypes = []
@@ -262,3 +265,59 @@ def kda_chunk_prefill_fwd(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound: 
     if rc != KDA_OK:
         detail = lib.kda_last_hip_error().decode() if rc == 4 else ""
         raise KdaError(rc, f"kda_chunk_prefill_fwd: {kda_status_string(rc)} {detail}".strip())
+
+
+def kda_spec_decode_step(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound: float, scale: float,
+                         state_pool, cu_seqlens, state_indices, num_accepted_tokens, out, workspace,
+                         stream=None) -> None:
+    """Queue one speculative-decode step with num_accepted_tokens rollback (see
+    include/kda.h, kda_spec_decode_step).
+
+    q, k, v, g, out [T, H, 128] bf16 (dense); beta_logits [T, H] bf16;
+    state_pool [num_slots, H, 128, 128] fp32 or bf16 (read and written in
+    place); cu_seqlens [N + 1] int32; state_indices [N, S] int32;
+    num_accepted_tokens [N] int32; workspace uint8.
+    """
+    import torch
+    lib = load_library()
+    if q.dim() != 3:
+        raise ValueError(f"q must be [T, H, {HEAD_DIM}], got {tuple(q.shape)}")
+    T, H, D = q.shape
+    if D != HEAD_DIM:
+        raise ValueError(f"head_dim must be {HEAD_DIM}, got {D}")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be [N + 1] with N >= 1")
+    N = cu_seqlens.numel() - 1
+    bf = torch.bfloat16
+    if state_pool.dtype == torch.float32:
+        sdt = KDA_STATE_FP32
+    elif state_pool.dtype == torch.bfloat16:
+        sdt = KDA_STATE_BF16
+    else:
+        raise TypeError(f"state dtype must be float32 or bfloat16, got {state_pool.dtype}")
+    if state_pool.dim() != 4:
+        raise ValueError("state_pool must be [num_slots, H, 128, 128]")
+    if state_indices.dim() != 2 or state_indices.shape[0] != N:
+        raise ValueError(f"state_indices must be [N, S] with N = {N}")
+    ptrs = [_check(t, n, bf, (T, H, D)) for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"))]
+    ptrs += [_check(beta_logits, "beta_logits", bf, (T, H)),
+             _check(_flat(A_log, "A_log", (H,)), "A_log", torch.float32, (H,)),
+             _check(_flat(dt_bias, "dt_bias", (H, D)), "dt_bias", torch.float32, (H, D))]
+    pool = _check(state_pool, "state_pool", state_pool.dtype,
+                  (state_pool.shape[0], H, HEAD_DIM, HEAD_DIM))
+    cu = _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    idx = _check(state_indices, "state_indices", torch.int32, tuple(state_indices.shape))
+    acc = _check(num_accepted_tokens, "num_accepted_tokens", torch.int32, (N,))
+    o = _check(out, "out", bf, (T, H, D))
+    ws = _check(workspace, "workspace", torch.uint8)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    rc = lib.kda_spec_decode_step(*ptrs, float(lower_bound), float(scale), pool,
+                                  int(state_pool.shape[0]), cu, idx, int(state_indices.shape[1]),
+                                  acc, o, ws, ctypes.c_void_p(int(stream)), T, H, N, sdt,
+                                  workspace.numel())
+    if rc != KDA_OK:
+        detail = lib.kda_last_hip_error().decode() if rc == 4 else ""
+        raise KdaError(rc, f"kda_spec_decode_step: {kda_status_string(rc)} {detail}".strip())

@@ -128,7 +128,8 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
                      void* stream, int64_t num_tokens, int32_t heads, int32_t num_seqs,
                      kda_state_dtype_t state_dtype, size_t workspace_bytes,
                      const kda_strides_t& sd, void* checkpoints = nullptr, int32_t ck_interval = 0,
-                     int64_t ck_capacity = 0) {
+                     int64_t ck_capacity = 0, const int32_t* sp_idx = nullptr,
+                     const int32_t* sp_acc = nullptr, int32_t sp_stride = 0, int64_t sp_slots = 0) {
   // ---- checks (no HIP call before they pass) --------------------------------
   if (num_tokens < 0 || num_tokens > INT32_MAX) return KDA_ERR_INVALID_ARG;  // int32 offsets
   // per-token tensors may be empty (and NULL) only when there are no tokens
@@ -157,6 +158,12 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   if (checkpoints) {
     if (ck_interval <= 0 || ck_interval % 16) return KDA_ERR_INVALID_ARG;
     if (ck_capacity < num_tokens / ck_interval) return KDA_ERR_INVALID_ARG;
+  }
+  if (sp_idx) {
+    if (!sp_acc || sp_stride <= 0 || sp_slots <= 0) return KDA_ERR_INVALID_ARG;
+    // slot offsets: sp_slots * heads * 128 * 128 elements
+    if (sp_slots > (INT64_MAX / 4) / (int64_t(heads) * KDA_HEAD_DIM * KDA_HEAD_DIM))
+      return KDA_ERR_INVALID_ARG;
   }
   const size_t need = kda_get_workspace_size(num_tokens, heads, num_seqs);
   if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
@@ -198,6 +205,10 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   p.ck = checkpoints;
   p.ck_int = ck_interval;
   p.ck_cap = ck_capacity;
+  p.sp_idx = sp_idx;
+  p.sp_acc = sp_acc;
+  p.sp_stride = sp_stride;
+  p.sp_slots = sp_slots;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   // kernel families: 4 the pipelined 16-token kernel (default for
@@ -211,6 +222,12 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   int kernel = override;
   if (kernel == 0)
     kernel = (!checkpoints && num_tokens <= kda::kDecodeTokensPerSeq * int64_t(num_seqs)) ? 3 : 4;
+  // a speculative-decode step runs on the token-serial kernels, which store
+  // the state after every token
+  if (sp_idx) {
+    if (override != 0 && override != 2 && override != 3) return KDA_ERR_UNSUPPORTED;
+    kernel = override == 2 ? 2 : 3;
+  }
   // the 16-token kernel takes lower_bound >= -5 and slices of <= 64 value
   // columns: below that bound the 32-token kernel, an unsplit launch (test
   // hook) the 64-token kernel.  Both pipelined kernels split the value
@@ -261,6 +278,23 @@ kda_status_t kda_chunk_prefill_fwd(const void* q, const void* k, const void* v, 
   return forward(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, scale, initial_state,
                  cu_seqlens, out, final_state, workspace, stream, num_tokens, heads, num_seqs,
                  state_dtype, workspace_bytes, dense);
+}
+
+kda_status_t kda_spec_decode_step(
+    const void* q, const void* k, const void* v, const void* g, const void* beta_logits,
+    const float* A_log, const float* dt_bias, float lower_bound, float scale, void* state_pool,
+    int64_t num_slots, const int32_t* cu_seqlens, const int32_t* state_indices,
+    int32_t indices_stride, const int32_t* num_accepted_tokens, void* out, void* workspace,
+    void* stream, int64_t num_tokens, int32_t heads, int32_t num_seqs,
+    kda_state_dtype_t state_dtype, size_t workspace_bytes) {
+  if (!state_pool || !state_indices) return KDA_ERR_INVALID_ARG;
+  const int64_t row = int64_t(heads) * KDA_HEAD_DIM;
+  const kda_strides_t dense{row, KDA_HEAD_DIM, row, KDA_HEAD_DIM, row,   KDA_HEAD_DIM,
+                            row, KDA_HEAD_DIM, heads, 1,          row, KDA_HEAD_DIM};
+  return forward(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, scale, state_pool,
+                 cu_seqlens, out, state_pool, workspace, stream, num_tokens, heads, num_seqs,
+                 state_dtype, workspace_bytes, dense, nullptr, 0, 0, state_indices,
+                 num_accepted_tokens, indices_stride, num_slots);
 }
 
 kda_status_t kda_chunk_prefill_fwd_checkpoints(

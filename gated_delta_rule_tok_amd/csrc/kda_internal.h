@@ -46,6 +46,16 @@ struct Params {
   void* ck;
   int ck_int;
   int64_t ck_cap;
+  // speculative-decode step (token-serial kernels only): null, or [N, sp_stride]
+  // state slots; sequence n starts from slot sp_idx[n][sp_acc[n] - 1] of the
+  // pool (s0 = sT = the pool, [sp_slots, H, D, D]) and stores the state after
+  // its t-th token in slot sp_idx[n][t].  Slots outside [0, sp_slots) read as
+  // the zero state and are not written; so are accepted counts outside
+  // [1, sp_stride] and tokens past sp_stride.
+  const int32_t* sp_idx;
+  const int32_t* sp_acc;
+  int sp_stride;
+  int64_t sp_slots;
 };
 
 // ---- bf16 helpers (bf16 is the high half of an IEEE fp32) -------------------

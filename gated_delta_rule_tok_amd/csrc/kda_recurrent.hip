@@ -26,6 +26,22 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// State row base of (sequence n, head h): the sequence's own state, or, in a
+// speculative-decode step, the pool slot it starts from (-1: the zero state).
+__device__ __forceinline__ int64_t start_slot(const Params& p, int n) {
+  if (!p.sp_idx) return n;
+  const int a = p.sp_acc[n];
+  if (a < 1 || a > p.sp_stride) return -1;
+  const int64_t s = p.sp_idx[int64_t(n) * p.sp_stride + a - 1];
+  return (s >= 0 && s < p.sp_slots) ? s : -1;
+}
+// The slot that receives the state after token i of sequence n's step (-1: none).
+__device__ __forceinline__ int64_t step_slot(const Params& p, int n, int i) {
+  if (i >= p.sp_stride) return -1;
+  const int64_t s = p.sp_idx[int64_t(n) * p.sp_stride + i];
+  return (s >= 0 && s < p.sp_slots) ? s : -1;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
@@ -63,14 +79,28 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(Params p) {
   const int r0 = rg * R;           // first key row
 
   float S[R];
+  const int64_t s0slot = start_slot(p, n);
   const size_t sbase = ((size_t)n * H + h) * kD * kD;
+  const size_t s0base = ((size_t)max(s0slot, int64_t(0)) * H + h) * kD * kD;
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    const size_t idx = sbase + (size_t)(r0 + i) * kD + j;
-    if (!p.s0) S[i] = 0.f;
+    const size_t idx = s0base + (size_t)(r0 + i) * kD + j;
+    if (!p.s0 || s0slot < 0) S[i] = 0.f;
     else if (p.state_bf16) S[i] = bf16_to_f32(static_cast<const uint16_t*>(p.s0)[idx]);
     else S[i] = static_cast<const float*>(p.s0)[idx];
   }
+  // the state after token i of a speculative-decode step, into its slot
+  auto store_step = [&](int i) {
+    const int64_t slot = step_slot(p, n, i);
+    if (slot < 0) return;
+    const size_t b = ((size_t)slot * H + h) * kD * kD;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const size_t idx = b + (size_t)(r0 + r) * kD + j;
+      if (p.state_bf16) static_cast<uint16_t*>(p.sT)[idx] = f32_to_bf16(S[r]);
+      else static_cast<float*>(p.sT)[idx] = S[r];
+    }
+  };
 
   const float eA = expf(p.A_log[h]);
   const float dtb0 = p.dt_bias[h * kD + 2 * lane];
@@ -159,10 +189,12 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(Params p) {
       }
       if (rg == 0)
         p.out[size_t(t0 + tt) * p.ts_o + size_t(h) * p.hs_o + j] = f32_to_bf16(fmaf(s_kq[tt], d, pq));
+      if (p.sp_idx) store_step(t0 + tt - bos);
     }
     __syncthreads();
   }
 
+  if (p.sp_idx) return;  // a speculative-decode step stores per token only
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const size_t idx = sbase + (size_t)(r0 + i) * kD + j;
@@ -207,11 +239,26 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p) {
   const int r0 = rg * R;              // first key row
 
   float4 S[R];
+  const int64_t s0slot = start_slot(p, n);
   const size_t sbase = ((size_t)n * H + h) * kD * kD;
+  const size_t s0base = ((size_t)max(s0slot, int64_t(0)) * H + h) * kD * kD;
+  // the state after token i of a speculative-decode step, into its slot
+  auto store_rows = [&](size_t b) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const size_t idx = b + (size_t)(r0 + i) * kD + j;
+      if (p.state_bf16) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.sT) + idx) =
+            uint2{pack_bf16x2(S[i].x, S[i].y), pack_bf16x2(S[i].z, S[i].w)};
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(p.sT) + idx) = S[i];
+      }
+    }
+  };
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    const size_t idx = sbase + (size_t)(r0 + i) * kD + j;
-    if (!p.s0) {
+    const size_t idx = s0base + (size_t)(r0 + i) * kD + j;
+    if (!p.s0 || s0slot < 0) {
       S[i] = float4{0.f, 0.f, 0.f, 0.f};
     } else if (p.state_bf16) {
       const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.s0) + idx);
@@ -311,20 +358,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p) {
                          pack_bf16x2(fmaf(kq, d.z, pq.z), fmaf(kq, d.w, pq.w))};
         *reinterpret_cast<uint2*>(p.out + size_t(t0 + tt) * p.ts_o + size_t(h) * p.hs_o + j) = o;
       }
+      if (p.sp_idx) {
+        const int64_t slot = step_slot(p, n, t0 + tt - bos);
+        if (slot >= 0) store_rows(((size_t)slot * H + h) * kD * kD);
+      }
     }
     __syncthreads();
   }
 
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const size_t idx = sbase + (size_t)(r0 + i) * kD + j;
-    if (p.state_bf16) {
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.sT) + idx) =
-          uint2{pack_bf16x2(S[i].x, S[i].y), pack_bf16x2(S[i].z, S[i].w)};
-    } else {
-      *reinterpret_cast<float4*>(static_cast<float*>(p.sT) + idx) = S[i];
-    }
-  }
+  if (!p.sp_idx) store_rows(sbase);  // a speculative-decode step stores per token only
 }
 
 }  // namespace

@@ -225,6 +225,53 @@ kda_status_t kda_chunk_prefill_fwd_checkpoints(
     kda_state_dtype_t state_dtype, size_t workspace_bytes, const kda_strides_t* strides,
     void* checkpoints, int32_t checkpoint_interval, int64_t checkpoint_capacity);
 
+/*
+ * One speculative-decode step with num_accepted_tokens rollback.  vLLM PR
+ * #55737's report (实现拆解 / "Implementation breakdown" item 4, and the
+ * spec-decode discussion under 评论区精华 / "Review highlights") keeps the
+ * speculative tokens on a per-token recurrent kernel "with num_accepted_tokens
+ * rollback semantics" without defining them; the reading implemented here:
+ *
+ *   Every sequence n of the step has L_n = cu[n+1] - cu[n] tokens (the
+ *   tokens it verifies).  It starts from the state stored after the last
+ *   token the previous step accepted: pool slot
+ *   state_indices[n][num_accepted_tokens[n] - 1].  It runs the recurrence of
+ *   kda_chunk_prefill_fwd over its tokens, writes out as that call does, and
+ *   stores the state after its i-th token (i = 0 .. L_n - 1) in pool slot
+ *   state_indices[n][i].  Rolling back to an accepted prefix of a tokens is
+ *   then the next step's num_accepted_tokens[n] = a: no state is recomputed.
+ *
+ *   state_pool           device, state dtype, [num_slots, heads, 128, 128]
+ *                        (row = key channel, as final_state); read and
+ *                        written in place
+ *   num_slots            slots in the pool (> 0)
+ *   state_indices        device int32 [num_seqs, indices_stride]
+ *   indices_stride       slots per sequence (> 0): the most tokens a sequence
+ *                        of the step stores a state for
+ *   num_accepted_tokens  device int32 [num_seqs]
+ *
+ * Device-side values are preconditions, not checked: an index outside
+ * [0, num_slots), or an accepted count outside [1, indices_stride], makes the
+ * sequence start from the zero state (for the start slot) or store nothing
+ * (for a token's slot); tokens past indices_stride store nothing.  A slot
+ * named by two sequences gives undefined results; the start slot may be
+ * among the sequence's own slots (every element is read before it is
+ * written).  The work runs on the token-serial decode kernel (4-token
+ * staging; the fp32 token-serial kernel under kda_debug_set_kernel(2)), with
+ * the arithmetic, the bit-identity across value splits and the other limits
+ * and guarantees of kda_chunk_prefill_fwd on dense tensors.  Returns
+ * KDA_ERR_INVALID_ARG for a NULL pool, indices or counts, or a non-positive
+ * num_slots or indices_stride, and KDA_ERR_UNSUPPORTED under a
+ * kda_debug_set_kernel override that selects a chunked kernel.
+ */
+kda_status_t kda_spec_decode_step(
+    const void* q, const void* k, const void* v, const void* g, const void* beta_logits,
+    const float* A_log, const float* dt_bias, float lower_bound, float scale, void* state_pool,
+    int64_t num_slots, const int32_t* cu_seqlens, const int32_t* state_indices,
+    int32_t indices_stride, const int32_t* num_accepted_tokens, void* out, void* workspace,
+    void* stream, int64_t num_tokens, int32_t heads, int32_t num_seqs,
+    kda_state_dtype_t state_dtype, size_t workspace_bytes);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* kda_status_string(kda_status_t status);
 

@@ -111,3 +111,65 @@ def kda_oracle_fwd(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, scale,
     if rc != 0:
         raise RuntimeError(f"kda_oracle_fwd failed with code {rc}")
     return out, fin
+
+
+def kda_oracle_spec_step(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, scale,
+                         state_pool, cu_seqlens, state_indices, num_accepted_tokens, *,
+                         threads=None):
+    """One speculative-decode step with num_accepted_tokens rollback, in fp64.
+
+    The reading (vLLM PR #55737's report, "Implementation breakdown" item 4
+    and the spec-decode discussion: the speculative tokens keep the per-token
+    recurrent kernel with its num_accepted_tokens rollback): sequence n starts
+    from pool slot state_indices[n][num_accepted_tokens[n] - 1] (the zero
+    state if that count or slot is out of range), runs the recurrence over its
+    tokens, and the state after its i-th token goes to slot
+    state_indices[n][i] (nothing for a slot out of range or i past the row).
+
+    Written as the definition: every state after token i is the final state
+    of kda_oracle_fwd over the sequence's first i + 1 tokens from the start
+    state; all start states are taken from the pool as it was before the
+    step.  state_pool: [S, H, 128, 128] float32, float64 or uint16 bf16 bits.
+    Returns (out float64 [T, H, 128], the pool after the step as float64).
+    """
+    q, k, v, g = (np.ascontiguousarray(x) for x in (q, k, v, g))
+    beta_logits = np.ascontiguousarray(beta_logits)
+    cu = np.asarray(cu_seqlens, np.int64)
+    idx = np.asarray(state_indices, np.int64)
+    acc = np.asarray(num_accepted_tokens, np.int64)
+    N, stride = idx.shape
+    pool = np.asarray(state_pool)
+    if pool.dtype == np.uint16:
+        pool = (pool.astype(np.uint32) << 16).view(np.float32)
+    pool = pool.astype(np.float64)
+    S, H = pool.shape[0], pool.shape[1]
+    T = q.shape[0]
+    out = np.zeros((T, H, HEAD_DIM), np.float64)
+    new_pool = pool.copy()
+    # one pseudo-sequence per (sequence, prefix length): the prefix's tokens,
+    # started from the sequence's start state
+    rows, lens, starts, dest = [], [], [], []
+    for n in range(N):
+        bos, eos = int(cu[n]), int(cu[n + 1])
+        a = int(acc[n])
+        slot = int(idx[n, a - 1]) if 1 <= a <= stride else -1
+        start = pool[slot] if 0 <= slot < S else np.zeros((H, HEAD_DIM, HEAD_DIM))
+        for i in range(eos - bos):
+            rows.append(np.arange(bos, bos + i + 1))
+            lens.append(i + 1)
+            starts.append(start)
+            dest.append((n, i, bos))
+    if not rows:
+        return out, new_pool
+    sel = np.concatenate(rows)
+    pcu = np.zeros(len(lens) + 1, np.int32)
+    pcu[1:] = np.cumsum(lens)
+    o, fin = kda_oracle_fwd(q[sel], k[sel], v[sel], g[sel], beta_logits[sel], A_log, dt_bias,
+                            lower_bound, scale, np.stack(starts), pcu, threads=threads)
+    for m, (n, i, bos) in enumerate(dest):
+        out[bos + i] = o[pcu[m + 1] - 1]       # the prefix's last token is token i
+        if i < stride:
+            slot = int(idx[n, i])
+            if 0 <= slot < S:
+                new_pool[slot] = fin[m]
+    return out, new_pool

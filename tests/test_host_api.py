@@ -33,7 +33,8 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == {"kda_get_workspace_size", "kda_chunk_prefill_fwd",
                           "kda_chunk_prefill_fwd_strided", "kda_chunk_prefill_fwd_checkpoints",
                           "kda_status_string",
-                          "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel"}
+                          "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel",
+                          "kda_spec_decode_step"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/kda.h but not exported"
 
@@ -263,3 +264,29 @@ def test_checkpoints_below_lower_bound_min_unsupported():
 def test_checkpoints_keep_the_forward_checks():
     assert _call_ck(q=None) == INVALID
     assert _call_ck(wsb=0) == WS_SMALL
+
+
+def _call_spec(**over):
+    """kda_spec_decode_step through ctypes (every call below is rejected before
+    any HIP call, so the fake pointers are never dereferenced)."""
+    lib = kda.load_library()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, lb=-5.0,
+             scale=128 ** -0.5, pool=FAKE, slots=16, cu=FAKE, idx=FAKE, stride=4, acc=FAKE,
+             out=FAKE, ws=FAKE, stream=None, T=8, H=2, N=2, sdt=0, wsb=1 << 20)
+    a.update(over)
+    return lib.kda_spec_decode_step(
+        a["q"], a["k"], a["v"], a["g"], a["beta"], a["A_log"], a["dt_bias"], a["lb"], a["scale"],
+        a["pool"], a["slots"], a["cu"], a["idx"], a["stride"], a["acc"], a["out"], a["ws"],
+        a["stream"], a["T"], a["H"], a["N"], a["sdt"], a["wsb"])
+
+
+@pytest.mark.parametrize("over", [dict(pool=None), dict(idx=None), dict(acc=None), dict(slots=0),
+                                  dict(slots=-3), dict(stride=0), dict(cu=None), dict(N=0),
+                                  dict(slots=2 ** 62)])
+def test_spec_step_argument_checks(over):
+    assert _call_spec(**over) == 1  # KDA_ERR_INVALID_ARG
+
+
+def test_spec_step_range_and_workspace_checks():
+    assert _call_spec(lb=-7.0) == 2        # KDA_ERR_UNSUPPORTED
+    assert _call_spec(wsb=0) == 3          # KDA_ERR_WORKSPACE_TOO_SMALL

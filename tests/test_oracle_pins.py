@@ -492,3 +492,80 @@ def test_pins_catch_planted_mistakes(oracle_mod):
         assert not survivors, f"mutants not caught by any pin: {survivors}"
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
+
+
+# ---- the speculative-decode step (kda_oracle_spec_step) --------------------------
+
+def _spec_inputs(lengths, heads, seed, slots):
+    x = KI.make_inputs(lengths, heads, seed=seed, init_state=None)
+    pool = (0.05 * np.random.default_rng(seed).standard_normal((slots, heads, D, D))).astype(np.float32)
+    return x, pool
+
+
+def test_spec_step_rollback_resumes_the_accepted_prefix():
+    """Rollback: a step verifying 4 draft tokens stores the state after each;
+    the next step, told that 2 were accepted, continues from the state after
+    the second.  Its output and states must equal the plain forward over the
+    accepted history (2 tokens of the first step, then the second step's)."""
+    x1, pool = _spec_inputs([4, 3], 2, seed=61, slots=10)
+    idx = np.array([[0, 1, 2, 3, 8], [4, 5, 6, 7, 9]], np.int32)
+    acc0 = np.array([5, 5], np.int32)       # both start from their last slot (8, 9)
+    o1, pool1 = oracle.kda_oracle_spec_step(x1.q, x1.k, x1.v, x1.g, x1.beta_logits, x1.A_log,
+                                            x1.dt_bias, x1.lower_bound, x1.scale, pool,
+                                            x1.cu_seqlens, idx, acc0)
+    x2 = KI.make_inputs([3, 2], 2, seed=62, init_state=None)
+    acc1 = np.array([2, 3], np.int32)       # 2 of the first sequence's, 3 of the second's
+    o2, pool2 = oracle.kda_oracle_spec_step(x2.q, x2.k, x2.v, x2.g, x2.beta_logits, x1.A_log,
+                                            x1.dt_bias, x1.lower_bound, x1.scale, pool1,
+                                            x2.cu_seqlens, idx, acc1)
+    for n, (a, start_slot) in enumerate(((2, 8), (3, 9))):
+        b1, b2 = int(x1.cu_seqlens[n]), int(x2.cu_seqlens[n])
+        L2 = int(x2.cu_seqlens[n + 1]) - b2
+        hist = lambda f1, f2: np.concatenate([f1[b1:b1 + a], f2[b2:b2 + L2]])
+        cu = np.array([0, a + L2], np.int32)
+        o, fin = oracle.kda_oracle_fwd(hist(x1.q, x2.q), hist(x1.k, x2.k), hist(x1.v, x2.v),
+                                       hist(x1.g, x2.g), hist(x1.beta_logits, x2.beta_logits),
+                                       x1.A_log, x1.dt_bias, x1.lower_bound, x1.scale,
+                                       pool[start_slot][None].astype(np.float64), cu)
+        np.testing.assert_allclose(o[:a], o1[b1:b1 + a], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(o[a:], o2[b2:b2 + L2], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(pool2[idx[n, L2 - 1]], fin[0], rtol=0, atol=1e-12)
+
+
+def test_spec_step_out_of_range_slots_and_counts():
+    """An accepted count outside [1, S] or an out-of-range slot gives the zero
+    start state; out-of-range destination slots and tokens past the row store
+    nothing; a start slot among the sequence's own slots is read before the
+    step writes it."""
+    x, pool = _spec_inputs([3, 2, 3], 1, seed=63, slots=6)
+    idx = np.array([[0, 1, -1], [2, 99, 3], [4, 5, 0]], np.int32)[:, :2]   # S = 2
+    idx = np.ascontiguousarray(idx)
+    acc = np.array([1, 0, 2], np.int32)     # seq 0 starts from slot 0 (its own first slot)
+    o, p = oracle.kda_oracle_spec_step(x.q, x.k, x.v, x.g, x.beta_logits, x.A_log, x.dt_bias,
+                                       x.lower_bound, x.scale, pool, x.cu_seqlens, idx, acc)
+
+    def run(n, start):
+        b, e = int(x.cu_seqlens[n]), int(x.cu_seqlens[n + 1])
+        outs, fins = [], []
+        for i in range(e - b):
+            oo, ff = oracle.kda_oracle_fwd(x.q[b:b + i + 1], x.k[b:b + i + 1], x.v[b:b + i + 1],
+                                           x.g[b:b + i + 1], x.beta_logits[b:b + i + 1],
+                                           x.A_log, x.dt_bias, x.lower_bound, x.scale,
+                                           start[None], np.array([0, i + 1], np.int32))
+            outs.append(oo[i])
+            fins.append(ff[0])
+        return outs, fins
+
+    zero = np.zeros((1, D, D))
+    o0, f0 = run(0, pool[0].astype(np.float64))       # slot 0 read before being overwritten
+    o1, f1 = run(1, zero)                             # accepted count 0: zero state
+    o2, f2 = run(2, pool[5].astype(np.float64))       # idx[2][1] = 5
+    np.testing.assert_allclose(o[0:3], np.stack(o0), atol=1e-12, rtol=0)
+    np.testing.assert_allclose(o[3:5], np.stack(o1), atol=1e-12, rtol=0)
+    np.testing.assert_allclose(o[5:8], np.stack(o2), atol=1e-12, rtol=0)
+    np.testing.assert_allclose(p[0], f0[0], atol=1e-12, rtol=0)   # seq 0, token 0
+    np.testing.assert_allclose(p[1], f0[1], atol=1e-12, rtol=0)   # token 1; token 2 has no slot
+    np.testing.assert_allclose(p[2], f1[0], atol=1e-12, rtol=0)   # seq 1 token 0; slot 99 ignored
+    np.testing.assert_allclose(p[4], f2[0], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(p[5], f2[1], atol=1e-12, rtol=0)
+    np.testing.assert_array_equal(p[3], pool[3].astype(np.float64))  # never named: untouched
