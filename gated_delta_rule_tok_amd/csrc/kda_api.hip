@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 
 #include "kda.h"
 #include "kda_internal.h"
@@ -29,6 +30,17 @@ std::atomic<int> g_cu_count[kMaxDevices];
 thread_local char t_last_hip_error[256] = "";
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// The integer a C caller passed for an enum parameter, read without loading it
+// as the enum type (a value outside the enumerators is then no undefined
+// behaviour, just an invalid argument).
+template <typename E>
+int enum_value(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "enum parameters are int-sized");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
 
 kda_status_t hip_failure(hipError_t e, const char* step) {
   std::snprintf(t_last_hip_error, sizeof t_last_hip_error, "%s (%s) during %s", hipGetErrorName(e),
@@ -79,7 +91,7 @@ size_t kda_get_workspace_size(int64_t max_tokens, int32_t heads, int32_t max_seq
 }
 
 const char* kda_status_string(kda_status_t status) {
-  switch (status) {
+  switch (enum_value(status)) {
     case KDA_OK: return "KDA_OK";
     case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: null pointer, bad size or bad scalar";
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: lower_bound outside the supported range";
@@ -126,8 +138,8 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
                      float lower_bound, float scale, const void* initial_state,
                      const int32_t* cu_seqlens, void* out, void* final_state, void* workspace,
                      void* stream, int64_t num_tokens, int32_t heads, int32_t num_seqs,
-                     kda_state_dtype_t state_dtype, size_t workspace_bytes,
-                     const kda_strides_t& sd, void* checkpoints = nullptr, int32_t ck_interval = 0,
+                     int sdt, size_t workspace_bytes, const kda_strides_t& sd,
+                     void* checkpoints = nullptr, int32_t ck_interval = 0,
                      int64_t ck_capacity = 0, const int32_t* sp_idx = nullptr,
                      const int32_t* sp_acc = nullptr, int32_t sp_stride = 0, int64_t sp_slots = 0) {
   // ---- checks (no HIP call before they pass) --------------------------------
@@ -152,7 +164,7 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   if (reinterpret_cast<uintptr_t>(beta_logits) % 2) return KDA_ERR_INVALID_ARG;
   // grid size: one workgroup per (sequence, head, value slice), up to 8 slices
   if (int64_t(num_seqs) * heads * 8 > INT32_MAX) return KDA_ERR_INVALID_ARG;
-  if (state_dtype != KDA_STATE_FP32 && state_dtype != KDA_STATE_BF16) return KDA_ERR_INVALID_ARG;
+  if (sdt != KDA_STATE_FP32 && sdt != KDA_STATE_BF16) return KDA_ERR_INVALID_ARG;
   if (!std::isfinite(lower_bound) || !std::isfinite(scale)) return KDA_ERR_INVALID_ARG;
   if (lower_bound > 0.f || lower_bound < KDA_LOWER_BOUND_MIN) return KDA_ERR_UNSUPPORTED;
   if (checkpoints) {
@@ -201,7 +213,7 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   p.H = heads;
   p.N = num_seqs;
   p.vsplit = s;
-  p.state_bf16 = state_dtype == KDA_STATE_BF16;
+  p.state_bf16 = sdt == KDA_STATE_BF16;
   p.ck = checkpoints;
   p.ck_int = ck_interval;
   p.ck_cap = ck_capacity;
@@ -277,7 +289,7 @@ kda_status_t kda_chunk_prefill_fwd(const void* q, const void* k, const void* v, 
                             row, KDA_HEAD_DIM, heads, 1,          row, KDA_HEAD_DIM};
   return forward(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, scale, initial_state,
                  cu_seqlens, out, final_state, workspace, stream, num_tokens, heads, num_seqs,
-                 state_dtype, workspace_bytes, dense);
+                 enum_value(state_dtype), workspace_bytes, dense);
 }
 
 kda_status_t kda_spec_decode_step(
@@ -293,7 +305,7 @@ kda_status_t kda_spec_decode_step(
                             row, KDA_HEAD_DIM, heads, 1,          row, KDA_HEAD_DIM};
   return forward(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, scale, state_pool,
                  cu_seqlens, out, state_pool, workspace, stream, num_tokens, heads, num_seqs,
-                 state_dtype, workspace_bytes, dense, nullptr, 0, 0, state_indices,
+                 enum_value(state_dtype), workspace_bytes, dense, nullptr, 0, 0, state_indices,
                  num_accepted_tokens, indices_stride, num_slots);
 }
 
@@ -310,7 +322,7 @@ kda_status_t kda_chunk_prefill_fwd_checkpoints(
                             row, KDA_HEAD_DIM, heads, 1,          row, KDA_HEAD_DIM};
   return forward(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, scale, initial_state,
                  cu_seqlens, out, final_state, workspace, stream, num_tokens, heads, num_seqs,
-                 state_dtype, workspace_bytes, strides ? *strides : dense, checkpoints,
+                 enum_value(state_dtype), workspace_bytes, strides ? *strides : dense, checkpoints,
                  checkpoint_interval, checkpoint_capacity);
 }
 
@@ -323,7 +335,7 @@ kda_status_t kda_chunk_prefill_fwd_strided(
   if (!strides) return KDA_ERR_INVALID_ARG;
   return forward(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, scale, initial_state,
                  cu_seqlens, out, final_state, workspace, stream, num_tokens, heads, num_seqs,
-                 state_dtype, workspace_bytes, *strides);
+                 enum_value(state_dtype), workspace_bytes, *strides);
 }
 
 }  // extern "C"

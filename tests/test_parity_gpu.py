@@ -381,3 +381,31 @@ def test_large_values(log2_scale, kernel):
         kda.kda_debug_set_kernel(prev)
     assert_parity(x, out, fin, oref, fref, label=f"|v| ~ 2^{log2_scale} kernel {kernel}",
                   relative=True)
+
+
+def test_kernel_choice_by_batch_average():
+    """The automatic choice goes by the batch's average length: the same
+    30-token sequence is served by the token-serial decode kernel when it is
+    batched with 40 one-token sequences (8 tokens per sequence or fewer on
+    average) and by the pipelined kernel when it comes alone.  Both results
+    follow the oracle; they need not be the same bits."""
+    import torch
+    big = KI.make_inputs([30] + [1] * 40, 2, seed=81, init_state="fp32")
+    rows = np.arange(0, 30)
+    alone = KI.make_inputs([30], 2, seed=81, init_state="fp32")
+    # the same 30-token sequence, initial state and parameters in both calls
+    for f in ("q", "k", "v", "g", "beta_logits"):
+        setattr(alone, f, getattr(big, f)[:30].copy())
+    alone.A_log, alone.dt_bias = big.A_log, big.dt_bias
+    alone.initial_state = big.initial_state[:1].copy()
+    assert big.T <= 8 * big.N and alone.T > 8 * alone.N
+    res = {}
+    for name, x in (("batched", big), ("alone", alone)):
+        d = to_device(x)
+        out, fin = run_gpu(x, d)
+        torch.cuda.synchronize()
+        oref, fref = run_oracle(x)
+        assert_parity(x, out, fin, oref, fref, label=f"30-token sequence {name}")
+        res[name] = (to_f64(out)[rows], to_f64(fin)[0])
+    d = np.abs(res["batched"][0] - res["alone"][0]).max()
+    print(f"[kernel choice] max |out batched - out alone| = {d:.3g}", flush=True)
