@@ -21,7 +21,7 @@ import os
 
 __all__ = ["kda_get_workspace_size", "kda_chunk_prefill_fwd", "kda_status_string",
            "kda_workspace_status",
-           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel", "kda_spec_decode_step", "KdaError", "library_path", "load_library"]
+           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel", "kda_spec_decode_step", "kda_chunk_prefill_fwd_noalloc", "KdaError", "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -87,6 +87,9 @@ def load_library():
             P, P, P, P, P, P, P, F, F, P, P, P, P, P, P, I64, I32, I32, ctypes.c_int, SZ,
             ctypes.POINTER(_Strides), P, I32, I64]
         lib.kda_chunk_prefill_fwd_checkpoints.restype = ctypes.c_int
+        lib.kda_chunk_prefill_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P, P, P, P,
+                                                      I64, I32, I32, ctypes.c_int]
+        lib.kda_chunk_prefill_fwd_noalloc.restype = ctypes.c_int
         lib.kda_spec_decode_step.argtypes = [P, P, P, P, P, P, P, F, F, P, I64, P, P, I32, P, P,
                                              P, P, I64, I32, I32, ctypes.c_int, SZ]
         lib.kda_spec_decode_step.restype = ctypes.c_int
@@ -321,3 +324,48 @@ def kda_spec_decode_step(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound: f
     if rc != KDA_OK:
         detail = lib.kda_last_hip_error().decode() if rc == 4 else ""
         raise KdaError(rc, f"kda_spec_decode_step: {kda_status_string(rc)} {detail}".strip())
+
+
+def kda_chunk_prefill_fwd_noalloc(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound: float,
+                                  scale: float, initial_state, cu_seqlens, out, final_state, status,
+                                  stream=None) -> None:
+    """kda_chunk_prefill_fwd without a workspace (see include/kda.h,
+    kda_chunk_prefill_fwd_noalloc): dense tensors as for the forward call;
+    status a device int32 tensor of one element (the status word)."""
+    import torch
+    lib = load_library()
+    if q.dim() != 3:
+        raise ValueError(f"q must be [T, H, {HEAD_DIM}], got {tuple(q.shape)}")
+    T, H, D = q.shape
+    if D != HEAD_DIM:
+        raise ValueError(f"head_dim must be {HEAD_DIM}, got {D}")
+    N = cu_seqlens.numel() - 1
+    if N < 1:
+        raise ValueError("cu_seqlens must be [N + 1] with N >= 1")
+    bf = torch.bfloat16
+    if final_state.dtype == torch.float32:
+        sdt = KDA_STATE_FP32
+    elif final_state.dtype == torch.bfloat16:
+        sdt = KDA_STATE_BF16
+    else:
+        raise TypeError(f"state dtype must be float32 or bfloat16, got {final_state.dtype}")
+    sshape = (N, H, HEAD_DIM, HEAD_DIM)
+    ptrs = [_check(t, n, bf, (T, H, D)) for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"))]
+    ptrs += [_check(beta_logits, "beta_logits", bf, (T, H)),
+             _check(_flat(A_log, "A_log", (H,)), "A_log", torch.float32, (H,)),
+             _check(_flat(dt_bias, "dt_bias", (H, D)), "dt_bias", torch.float32, (H, D))]
+    s0 = None if initial_state is None else _check(initial_state, "initial_state",
+                                                   final_state.dtype, sshape)
+    cu = _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    o = _check(out, "out", bf, (T, H, D))
+    fs = _check(final_state, "final_state", final_state.dtype, sshape)
+    st = _check(status, "status", torch.int32, (1,))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    rc = lib.kda_chunk_prefill_fwd_noalloc(*ptrs, float(lower_bound), float(scale), s0, cu, o, fs, st,
+                                           ctypes.c_void_p(int(stream)), T, H, N, sdt)
+    if rc != KDA_OK:
+        detail = lib.kda_last_hip_error().decode() if rc == 4 else ""
+        raise KdaError(rc, f"kda_chunk_prefill_fwd_noalloc: {kda_status_string(rc)} {detail}".strip())

@@ -29,6 +29,30 @@ std::atomic<int> g_cu_count[kMaxDevices];
 
 thread_local char t_last_hip_error[256] = "";
 
+// Scratch of kda_chunk_prefill_fwd_noalloc (for callers that cannot
+// allocate): the sequence order table, kNoAllocMaxSeqs entries, one copy per
+// device for the life of the process.  Host code never uses the array's name
+// as an address: its device address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+constexpr int kNoAllocMaxSeqs = 65536;
+static __device__ __align__(256) int32_t scratch[kNoAllocMaxSeqs];
+std::atomic<int32_t*> g_scratch[kMaxDevices];
+
+hipError_t scratch_address(int32_t** out) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int32_t* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    if (hipError_t e = hipGetSymbolAddress(reinterpret_cast<void**>(&ptr), HIP_SYMBOL(scratch));
+        e != hipSuccess)
+      return e;
+    g_scratch[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return hipSuccess;
+}
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // The integer a C caller passed for an enum parameter, read without loading it
@@ -141,7 +165,8 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
                      int sdt, size_t workspace_bytes, const kda_strides_t& sd,
                      void* checkpoints = nullptr, int32_t ck_interval = 0,
                      int64_t ck_capacity = 0, const int32_t* sp_idx = nullptr,
-                     const int32_t* sp_acc = nullptr, int32_t sp_stride = 0, int64_t sp_slots = 0) {
+                     const int32_t* sp_acc = nullptr, int32_t sp_stride = 0, int64_t sp_slots = 0,
+                     int32_t* fixed_status = nullptr, bool fixed_scratch = false) {
   // ---- checks (no HIP call before they pass) --------------------------------
   if (num_tokens < 0 || num_tokens > INT32_MAX) return KDA_ERR_INVALID_ARG;  // int32 offsets
   // per-token tensors may be empty (and NULL) only when there are no tokens
@@ -177,9 +202,16 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
     if (sp_slots > (INT64_MAX / 4) / (int64_t(heads) * KDA_HEAD_DIM * KDA_HEAD_DIM))
       return KDA_ERR_INVALID_ARG;
   }
-  const size_t need = kda_get_workspace_size(num_tokens, heads, num_seqs);
-  if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
-  if (need > 0 && !workspace) return KDA_ERR_INVALID_ARG;
+  if (fixed_scratch) {
+    // no workspace: the status word is the caller's, the order table the
+    // library's static scratch
+    if (!fixed_status) return KDA_ERR_INVALID_ARG;
+    if (num_seqs > kNoAllocMaxSeqs) return KDA_ERR_INVALID_ARG;
+  } else {
+    const size_t need = kda_get_workspace_size(num_tokens, heads, num_seqs);
+    if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (need > 0 && !workspace) return KDA_ERR_INVALID_ARG;
+  }
 
   // ---- plan --------------------------------------------------------------------
   int cus = 0;
@@ -199,8 +231,14 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   p.sT = final_state;
   p.out = static_cast<uint16_t*>(out);
   p.cu = cu_seqlens;
-  p.errword = static_cast<int32_t*>(workspace);
-  p.order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kAlign);
+  if (fixed_scratch) {
+    p.errword = fixed_status;
+    if (hipError_t e = scratch_address(&p.order); e != hipSuccess)
+      return hip_failure(e, "scratch address query");
+  } else {
+    p.errword = static_cast<int32_t*>(workspace);
+    p.order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kAlign);
+  }
   p.lower_bound = lower_bound;
   p.scale = scale;
   p.ts_q = int(sd.q_token), p.hs_q = int(sd.q_head);
@@ -290,6 +328,21 @@ kda_status_t kda_chunk_prefill_fwd(const void* q, const void* k, const void* v, 
   return forward(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, scale, initial_state,
                  cu_seqlens, out, final_state, workspace, stream, num_tokens, heads, num_seqs,
                  enum_value(state_dtype), workspace_bytes, dense);
+}
+
+kda_status_t kda_chunk_prefill_fwd_noalloc(
+    const void* q, const void* k, const void* v, const void* g, const void* beta_logits,
+    const float* A_log, const float* dt_bias, float lower_bound, float scale,
+    const void* initial_state, const int32_t* cu_seqlens, void* out, void* final_state,
+    int32_t* status, void* stream, int64_t num_tokens, int32_t heads, int32_t num_seqs,
+    kda_state_dtype_t state_dtype) {
+  const int64_t row = int64_t(heads) * KDA_HEAD_DIM;
+  const kda_strides_t dense{row, KDA_HEAD_DIM, row, KDA_HEAD_DIM, row,   KDA_HEAD_DIM,
+                            row, KDA_HEAD_DIM, heads, 1,          row, KDA_HEAD_DIM};
+  return forward(q, k, v, g, beta_logits, A_log, dt_bias, lower_bound, scale, initial_state,
+                 cu_seqlens, out, final_state, nullptr, stream, num_tokens, heads, num_seqs,
+                 enum_value(state_dtype), 0, dense, nullptr, 0, 0, nullptr, nullptr, 0, 0, status,
+                 true);
 }
 
 kda_status_t kda_spec_decode_step(

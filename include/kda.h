@@ -226,6 +226,34 @@ kda_status_t kda_chunk_prefill_fwd_checkpoints(
     void* checkpoints, int32_t checkpoint_interval, int64_t checkpoint_capacity);
 
 /*
+ * kda_chunk_prefill_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops or harnesses that forbid
+ * allocation): no workspace argument.  The sequence order table, the one
+ * scratch buffer of the call (written by a ranking kernel when num_seqs > 16,
+ * then read by the forward kernel), lives in a static device array of the
+ * library, 65536 entries (256 KiB) per device, held until the process ends;
+ * its device address is queried once per device (hipGetSymbolAddress), and the
+ * call allocates nothing.
+ *
+ *   status    device int32 (required): the status word of the workspace
+ *             contract (zero it before the first call; nonzero after the work
+ *             completes if a kernel gave up a bounded wait).
+ *
+ * Limits: num_seqs <= 65536 (else KDA_ERR_INVALID_ARG).  Every call on one
+ * device shares that device's table, which keeps the last call's contents:
+ * calls that may overlap on one device (different streams without ordering
+ * between them) race on it and give undefined results.  Every other argument,
+ * limit and guarantee is that of kda_chunk_prefill_fwd on dense tensors, with
+ * the same results bit for bit.
+ */
+kda_status_t kda_chunk_prefill_fwd_noalloc(
+    const void* q, const void* k, const void* v, const void* g, const void* beta_logits,
+    const float* A_log, const float* dt_bias, float lower_bound, float scale,
+    const void* initial_state, const int32_t* cu_seqlens, void* out, void* final_state,
+    int32_t* status, void* stream, int64_t num_tokens, int32_t heads, int32_t num_seqs,
+    kda_state_dtype_t state_dtype);
+
+/*
  * One speculative-decode step with num_accepted_tokens rollback.  vLLM PR
  * #55737's report (实现拆解 / "Implementation breakdown" item 4, and the
  * spec-decode discussion under 评论区精华 / "Review highlights") keeps the

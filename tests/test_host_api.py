@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
                           "kda_chunk_prefill_fwd_strided", "kda_chunk_prefill_fwd_checkpoints",
                           "kda_status_string",
                           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel",
-                          "kda_spec_decode_step"}
+                          "kda_spec_decode_step", "kda_chunk_prefill_fwd_noalloc"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/kda.h but not exported"
 
