@@ -88,8 +88,13 @@ def traffic_from_pmc(pmc_dir: str, workload: str, command: str, kernel: str) -> 
     launch of the dominant kernel.  Expects pmc_dir/{fetch,write,cal_fetch,cal_write}/
     run_counter_collection.csv; the calibration copy moves 256 MiB."""
     f = lambda d: os.path.join(pmc_dir, d, "run_counter_collection.csv")
-    fetch, nf = _pmc_sum(f("fetch"), kernel)
-    write, nw = _pmc_sum(f("write"), kernel)
+    # "a+b": one call launches both kernels; its bytes are the sum of their means
+    fetch = write = 0.0
+    nf = nw = 0
+    for k in kernel.split("+"):
+        fk, nfk = _pmc_sum(f("fetch"), k)
+        wk, nwk = _pmc_sum(f("write"), k)
+        fetch, write, nf, nw = fetch + fk, write + wk, nf + nfk, nw + nwk
     cal_f, _ = _pmc_sum(f("cal_fetch"), "copyBuffer")
     cal_w, _ = _pmc_sum(f("cal_write"), "copyBuffer")
     copy_kib = 256 * 1024
@@ -105,9 +110,14 @@ def traffic_from_pmc(pmc_dir: str, workload: str, command: str, kernel: str) -> 
     return out
 
 
+PROJ_KERNELS = "proj_ab_kernel+proj_out_kernel"
+
+
 def workload_name(args):
     """(workload name, dominant kernel, the selecting arguments) of a run."""
     import kda_inputs as KI
+    if getattr(args, "proj", 0):
+        return f"proj_{args.proj}x7168_144_1536", PROJ_KERNELS, f"--proj {args.proj}"
     if args.decode_batch:
         wl, lb = f"decode_{args.decode_batch}x1_h16", KI.LOWER_BOUND
         sel = f"--decode-batch {args.decode_batch}"
@@ -119,6 +129,148 @@ def workload_name(args):
         wl += f"_lb{args.lower_bound:g}"
         sel += f" --lower-bound {args.lower_bound:g}"
     return wl, dominant_kernel(bool(args.decode_batch), lb), sel
+
+
+PROJ_K, PROJ_NAB, PROJ_NB = 7168, 144, 1536
+
+
+def proj_algorithmic_bytes(M, K=PROJ_K, n_ab=PROJ_NAB, n_b=PROJ_NB):
+    """Bytes the two projections must move: hidden and both weights read once,
+    P and G written once (bf16)."""
+    return 2 * (M * K + n_ab * K + n_b * 128 + M * n_ab + M * n_b)
+
+
+def bench_proj(args):
+    """Time kda_gate_proj (both kernels of one call) for args.proj tokens.
+    Weight sets are rotated so that the weights come from HBM, as for a layer
+    whose weights were last read a whole model pass ago: 128 sets of 2.4 MB
+    exceed the 256 MB last-level cache.  The launch time is the call's (both
+    kernels, events on the launch stream); the roofline is its algorithmic
+    bytes against 8 TB/s."""
+    import torch
+    import gated_delta_rule_tok_amd as kda
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M, K, NAB, NB = args.proj, PROJ_K, PROJ_NAB, PROJ_NB
+    nsets = 128
+    rng = np.random.default_rng(11)
+    import kda_inputs as KI
+    h_np = KI.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    wab_np = KI.f32_to_bf16_bits((K ** -0.5 * rng.standard_normal((NAB, K))).astype(np.float32))
+    wb_np = KI.f32_to_bf16_bits((128 ** -0.5 * rng.standard_normal((NB, 128))).astype(np.float32))
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    h0, wab0, wb0 = bf(h_np), bf(wab_np), bf(wb_np)
+    sets = []
+    for i in range(nsets):
+        sets.append(dict(h=h0.clone(), wab=wab0.clone(), wb=wb0.clone(),
+                         p=torch.empty(M, NAB, dtype=torch.bfloat16, device=dev),
+                         g=torch.empty(M, NB, dtype=torch.bfloat16, device=dev),
+                         ws=torch.zeros(kda.kda_gate_proj_workspace_size(M, K, NAB),
+                                        dtype=torch.uint8, device=dev)))
+
+    def step(i):
+        s = sets[i % nsets]
+        kda.kda_gate_proj(s["h"], s["wab"], s["wb"], s["p"], s["g"], s["ws"])
+
+    stream = torch.cuda.current_stream()
+    c0, n = time.perf_counter(), 0
+    while time.perf_counter() - c0 < args.settle_ms * 1e-3:
+        for _ in range(64):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    # one graph holding 64 calls (64 weight sets): device time per call with no
+    # host work and no per-launch submission gap between calls
+    graph_us = None
+    if not args.no_graph:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(64):
+                    s = sets[i]
+                    kda.kda_gate_proj(s["h"], s["wab"], s["wb"], s["p"], s["g"], s["ws"],
+                                      stream=cap)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(10)]
+        for a, b in gev:
+            a.record(stream)
+            graph.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        graph_us = float(np.median([a.elapsed_time(b) for a, b in gev])) * 1e3 / 64
+
+    ms_per_step = wall * 1e3 / args.steps
+    launch_ms = float(call_ms.mean())
+    abytes = proj_algorithmic_bytes(M)
+    traffic = None
+    wl, _, _ = workload_name(args)
+    tf = traffic_file(wl, PROJ_KERNELS)
+    if os.path.exists(tf):
+        t = json.load(open(tf))
+        if t.get("kernel_source_sha256") == kernel_source_hash():
+            traffic = t["bytes_per_launch"]
+    achieved = abytes / (launch_ms * 1e-3) / 1e9
+    result = {
+        "metric": "KDA gate / beta projection tokens/s (hidden 7168 -> 144 -> 1536)",
+        "value": M / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "us_per_call_event_median": float(np.median(call_ms)) * 1e3,
+        "us_per_call_event_min": float(call_ms.min()) * 1e3,
+        "us_per_call_graph_replay": graph_us,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl, "tokens": M, "hidden": K,
+                   "n_ab": NAB, "n_b": NB, "weight_sets": nsets},
+        "roofline": {"bound": "hbm", "kernel": PROJ_KERNELS,
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": abytes, "launch_us": launch_ms * 1e3,
+                     "graph_frac": (abytes / (graph_us * 1e-6) / 1e9 / HBM_PEAK_GBS
+                                    if graph_us else None)},
+    }
+    if not args.no_cpu:
+        from oracle import proj
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # noqa: BLE001 - thread count is informational
+            threads = 1
+        times = []
+        while len(times) < 50 and sum(times) < 3.0:
+            c0 = time.perf_counter()
+            proj.gate_proj(h_np, wab_np, wb_np)
+            times.append(time.perf_counter() - c0)
+        cpu_s = float(np.median(times))
+        result["cpu_baseline"] = {
+            "value": M / cpu_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole call ({M} tokens), fp64 numpy products; median of "
+                      f"{len(times)} calls, {cpu_s * 1e3:.2f} ms each"}
+    print(json.dumps(result), flush=True)
 
 
 def main():
@@ -143,6 +295,9 @@ def main():
                     help="run the call this long before the warmup steps (clock ramp; 0: none)")
     ap.add_argument("--traffic-from", metavar="PMC_DIR",
                     help="write the traffic file for --config from rocprofv3 counter runs, then exit")
+    ap.add_argument("--proj", type=int, default=0, metavar="M",
+                    help="instead of the forward: time the gate / beta projections (kda_gate_proj) "
+                         "for M tokens at hidden 7168, 144 = 128 + 16 rows, 1536 gate columns")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy three times (the counter calibration), then exit")
     args = ap.parse_args()
@@ -177,6 +332,10 @@ def main():
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
               "the KDA forward has no cross-GPU path here", file=sys.stderr)
         sys.exit(2)
+
+    if args.proj:
+        bench_proj(args)
+        return
 
     import torch
     import kda_inputs as KI

@@ -21,7 +21,8 @@ import os
 
 __all__ = ["kda_get_workspace_size", "kda_chunk_prefill_fwd", "kda_status_string",
            "kda_workspace_status",
-           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel", "kda_spec_decode_step", "kda_chunk_prefill_fwd_noalloc", "KdaError", "library_path", "load_library"]
+           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel", "kda_spec_decode_step", "kda_chunk_prefill_fwd_noalloc", "kda_gate_proj",
+           "kda_gate_proj_workspace_size", "KdaError", "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -90,6 +91,10 @@ def load_library():
         lib.kda_chunk_prefill_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, F, F, P, P, P, P, P, P,
                                                       I64, I32, I32, ctypes.c_int]
         lib.kda_chunk_prefill_fwd_noalloc.restype = ctypes.c_int
+        lib.kda_gate_proj_workspace_size.argtypes = [I32, I32, I32]
+        lib.kda_gate_proj_workspace_size.restype = SZ
+        lib.kda_gate_proj.argtypes = [P, P, P, P, P, P, SZ, P, I32, I32, I32, I32]
+        lib.kda_gate_proj.restype = ctypes.c_int
         lib.kda_spec_decode_step.argtypes = [P, P, P, P, P, P, P, F, F, P, I64, P, P, I32, P, P,
                                              P, P, I64, I32, I32, ctypes.c_int, SZ]
         lib.kda_spec_decode_step.restype = ctypes.c_int
@@ -369,3 +374,36 @@ def kda_chunk_prefill_fwd_noalloc(q, k, v, g, beta_logits, A_log, dt_bias, lower
     if rc != KDA_OK:
         detail = lib.kda_last_hip_error().decode() if rc == 4 else ""
         raise KdaError(rc, f"kda_chunk_prefill_fwd_noalloc: {kda_status_string(rc)} {detail}".strip())
+
+
+def kda_gate_proj_workspace_size(num_tokens: int, hidden_dim: int, n_ab: int) -> int:
+    return int(load_library().kda_gate_proj_workspace_size(int(num_tokens), int(hidden_dim),
+                                                             int(n_ab)))
+
+
+def kda_gate_proj(hidden, w_ab, w_b, p_ab, g, workspace, stream=None) -> None:
+    """Queue the gate / beta projections (see include/kda.h, kda_gate_proj):
+    P = bf16(hidden w_ab^T) into p_ab [M, n_ab], G = bf16(P[:, :128] w_b^T)
+    into g [M, n_b] (or a [M, n_b / 128, 128] view).  bf16 tensors, dense;
+    workspace uint8 of kda_gate_proj_workspace_size bytes (no initialisation
+    needed)."""
+    import torch
+    lib = load_library()
+    bf = torch.bfloat16
+    if hidden.dim() != 2 or w_ab.dim() != 2 or w_b.dim() != 2:
+        raise ValueError("hidden, w_ab and w_b must be 2-D")
+    M, K = hidden.shape
+    n_ab, n_b = w_ab.shape[0], w_b.shape[0]
+    ptrs = [_check(hidden, "hidden", bf, (M, K)), _check(w_ab, "w_ab", bf, (n_ab, K)),
+            _check(w_b, "w_b", bf, (n_b, 128)), _check(p_ab, "p_ab", bf, (M, n_ab)),
+            _check(g.reshape(M, n_b) if g.is_contiguous() else g, "g", bf, (M, n_b))]
+    ws = _check(workspace, "workspace", torch.uint8)
+    if stream is None:
+        stream = torch.cuda.current_stream(hidden.device).cuda_stream
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    rc = lib.kda_gate_proj(*ptrs, ws, workspace.numel(), ctypes.c_void_p(int(stream)), M, K, n_ab,
+                           n_b)
+    if rc != KDA_OK:
+        detail = lib.kda_last_hip_error().decode() if rc == 4 else ""
+        raise KdaError(rc, f"kda_gate_proj: {kda_status_string(rc)} {detail}".strip())

@@ -330,6 +330,46 @@ kda_status_t kda_chunk_prefill_fwd(const void* q, const void* k, const void* v, 
                  enum_value(state_dtype), workspace_bytes, dense);
 }
 
+size_t kda_gate_proj_workspace_size(int32_t num_tokens, int32_t hidden_dim, int32_t n_ab) {
+  if (num_tokens < 0 || hidden_dim <= 0 || n_ab <= 0) return 0;
+  return kda::proj_workspace_bytes(num_tokens, hidden_dim, n_ab);
+}
+
+kda_status_t kda_gate_proj(const void* hidden, const void* w_ab, const void* w_b, void* p_ab,
+                           void* g, void* workspace, size_t workspace_bytes, void* stream,
+                           int32_t num_tokens, int32_t hidden_dim, int32_t n_ab, int32_t n_b) {
+  // ---- checks (no HIP call before they pass) --------------------------------
+  if (num_tokens < 0 || num_tokens > (1 << 16)) return KDA_ERR_INVALID_ARG;
+  if (hidden_dim <= 0 || hidden_dim % 8 || hidden_dim > (1 << 24)) return KDA_ERR_INVALID_ARG;
+  if (n_ab < kda::kProjRank || n_ab % 8 || n_ab > 4096) return KDA_ERR_INVALID_ARG;
+  if (n_b <= 0 || n_b % 16 || n_b > (1 << 20)) return KDA_ERR_INVALID_ARG;
+  if (!w_ab || !w_b) return KDA_ERR_INVALID_ARG;
+  if (num_tokens > 0 && (!hidden || !p_ab || !g)) return KDA_ERR_INVALID_ARG;
+  for (const void* ptr : {hidden, w_ab, w_b, static_cast<const void*>(p_ab)})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16) return KDA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(g) % 2) return KDA_ERR_INVALID_ARG;
+  const size_t need = kda_gate_proj_workspace_size(num_tokens, hidden_dim, n_ab);
+  if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return KDA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(workspace) % 16) return KDA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return KDA_OK;
+
+  kda::ProjParams pp{};
+  pp.hidden = static_cast<const uint16_t*>(hidden);
+  pp.w_ab = static_cast<const uint16_t*>(w_ab);
+  pp.w_b = static_cast<const uint16_t*>(w_b);
+  pp.p_ab = static_cast<uint16_t*>(p_ab);
+  pp.g = static_cast<uint16_t*>(g);
+  pp.partials = static_cast<float*>(workspace);
+  pp.M = num_tokens;
+  pp.K = hidden_dim;
+  pp.n_ab = n_ab;
+  pp.n_b = n_b;
+  if (hipError_t e = kda::launch_proj(pp, static_cast<hipStream_t>(stream)); e != hipSuccess)
+    return hip_failure(e, "projection launch");
+  return KDA_OK;
+}
+
 kda_status_t kda_chunk_prefill_fwd_noalloc(
     const void* q, const void* k, const void* v, const void* g, const void* beta_logits,
     const float* A_log, const float* dt_bias, float lower_bound, float scale,

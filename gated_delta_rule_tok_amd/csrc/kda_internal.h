@@ -125,4 +125,22 @@ hipError_t launch_pipe(const Params& p, hipStream_t stream);
 // itself.
 hipError_t launch_fwd32(const Params& p, hipStream_t stream);
 
+// ---- the gate / beta projections (kda_proj.hip) ---------------------------------
+constexpr int kProjRank = 128;  // inner dimension of the gate's second factor
+// Row-major bf16 matrices: hidden [M, K], w_ab [n_ab, K], w_b [n_b, 128];
+// outputs p_ab [M, n_ab], g [M, n_b].  partials: the workspace
+// (proj_workspace_bytes), written before it is read in every call.
+struct ProjParams {
+  const uint16_t* hidden;
+  const uint16_t* w_ab;
+  const uint16_t* w_b;
+  uint16_t* p_ab;
+  uint16_t* g;
+  float* partials;
+  int M, K, n_ab, n_b;
+};
+size_t proj_workspace_bytes(int M, int K, int n_ab);
+// Two launches: P = bf16(hidden w_ab^T), then G = bf16(P[:, :128] w_b^T).
+hipError_t launch_proj(const ProjParams& p, hipStream_t stream);
+
 }  // namespace kda

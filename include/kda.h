@@ -300,6 +300,48 @@ kda_status_t kda_spec_decode_step(
     void* stream, int64_t num_tokens, int32_t heads, int32_t num_seqs,
     kda_state_dtype_t state_dtype, size_t workspace_bytes);
 
+/*
+ * The gate and beta projections upstream of the forward, for few tokens (a
+ * decode step): the skinny N and K GEMMs of the PR #55426 report ("Fix KDA
+ * projection overlap on Hopper", "Implementation breakdown" items 1-3 and
+ * "Key source snippets"), bf16 operands with fp32 accumulation:
+ *
+ *   P = round_bf16(hidden x w_ab^T)          [num_tokens, n_ab]
+ *   G = round_bf16(P[:, :128] x w_b^T)       [num_tokens, n_b]
+ *
+ * w_ab stacks the gate's first factor (rows 0..127, the rank-128 F_A) over
+ * the beta rows (128..n_ab-1); w_b is the gate's second factor (F_B).  The
+ * page's test shapes: hidden_dim 7168, n_ab 144, n_b 1536 (12 heads of 128),
+ * 2..14 tokens.  G is the forward's raw gate input g [num_tokens, n_b / 128,
+ * 128] as it stands, and P's columns 128.. are its raw beta logits: pass them
+ * to kda_chunk_prefill_fwd_strided as the column slice P + 128 with
+ * beta_token = n_ab, beta_head = 1.  Rounding is to nearest even.  The sum
+ * over hidden_dim runs in 1024-wide slices (four 256-wide quarters added in
+ * order) whose fp32 partials are added in slice order, so results are
+ * run-to-run deterministic.
+ *
+ *   hidden     device bf16 [num_tokens, hidden_dim], dense
+ *   w_ab       device bf16 [n_ab, hidden_dim], dense
+ *   w_b        device bf16 [n_b, 128], dense
+ *   p_ab, g    device bf16 outputs [num_tokens, n_ab], [num_tokens, n_b]
+ *   workspace  device, at least kda_gate_proj_workspace_size(num_tokens,
+ *              hidden_dim, n_ab) bytes (partial sums over K slices, written
+ *              before they are read: no initialisation needed); calls that
+ *              may overlap need workspaces of their own
+ *   limits     hidden_dim a positive multiple of 8 (at most 2^24), n_ab a
+ *              multiple of 8 in [128, 4096], n_b a positive multiple of 16,
+ *              num_tokens in [0, 65536]; hidden, w_ab, w_b, p_ab and the
+ *              workspace 16-byte aligned
+ *
+ * Queued on `stream` (two kernels), no allocation, no host synchronisation.
+ * Returns KDA_ERR_INVALID_ARG / KDA_ERR_WORKSPACE_TOO_SMALL before any HIP
+ * call, KDA_ERR_HIP if a launch fails.
+ */
+size_t kda_gate_proj_workspace_size(int32_t num_tokens, int32_t hidden_dim, int32_t n_ab);
+kda_status_t kda_gate_proj(const void* hidden, const void* w_ab, const void* w_b, void* p_ab,
+                           void* g, void* workspace, size_t workspace_bytes, void* stream,
+                           int32_t num_tokens, int32_t hidden_dim, int32_t n_ab, int32_t n_b);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* kda_status_string(kda_status_t status);
 

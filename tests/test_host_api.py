@@ -34,7 +34,8 @@ def test_library_exports_every_declared_symbol():
                           "kda_chunk_prefill_fwd_strided", "kda_chunk_prefill_fwd_checkpoints",
                           "kda_status_string",
                           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel",
-                          "kda_spec_decode_step", "kda_chunk_prefill_fwd_noalloc"}
+                          "kda_spec_decode_step", "kda_chunk_prefill_fwd_noalloc",
+                          "kda_gate_proj", "kda_gate_proj_workspace_size"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/kda.h but not exported"
 
@@ -290,3 +291,31 @@ def test_spec_step_argument_checks(over):
 def test_spec_step_range_and_workspace_checks():
     assert _call_spec(lb=-7.0) == 2        # KDA_ERR_UNSUPPORTED
     assert _call_spec(wsb=0) == 3          # KDA_ERR_WORKSPACE_TOO_SMALL
+
+
+
+def _call_proj(**over):
+    lib = kda.load_library()
+    a = dict(hidden=FAKE, w_ab=FAKE, w_b=FAKE, p_ab=FAKE, g=FAKE, ws=FAKE, wsb=1 << 22, stream=None,
+             M=8, K=7168, n_ab=144, n_b=1536)
+    a.update(over)
+    return lib.kda_gate_proj(a["hidden"], a["w_ab"], a["w_b"], a["p_ab"], a["g"], a["ws"], a["wsb"],
+                             a["stream"], a["M"], a["K"], a["n_ab"], a["n_b"])
+
+
+@pytest.mark.parametrize("over", [dict(hidden=None), dict(w_ab=None), dict(w_b=None), dict(g=None),
+                                  dict(p_ab=None), dict(ws=None), dict(M=-1), dict(M=65537), dict(K=0), dict(K=7170),
+                                  dict(n_ab=120), dict(n_ab=146), dict(n_b=1544), dict(n_b=0),
+                                  dict(hidden=ctypes.c_void_p(0x1008))])
+def test_proj_argument_checks(over):
+    assert _call_proj(**over) == INVALID
+
+
+def test_proj_workspace_checks():
+    need = kda.kda_gate_proj_workspace_size(8, 7168, 144)
+    # one fp32 16 x 16 partial tile per (1024-wide K slice, 16 rows of w_ab, 16 tokens)
+    assert need == 7 * 9 * 256 * 4
+    assert _call_proj(wsb=need - 1) == WS_SMALL
+    assert kda.kda_gate_proj_workspace_size(-1, 7168, 144) == 0
+    assert kda.kda_gate_proj_workspace_size(17, 7168, 144) == 2 * 7 * 9 * 256 * 4  # two token tiles
+    assert kda.kda_gate_proj_workspace_size(5, 1000, 136) == 1 * 9 * 256 * 4       # ragged K and n_ab

@@ -569,3 +569,84 @@ def test_spec_step_out_of_range_slots_and_counts():
     np.testing.assert_allclose(p[4], f2[0], atol=1e-12, rtol=0)
     np.testing.assert_allclose(p[5], f2[1], atol=1e-12, rtol=0)
     np.testing.assert_array_equal(p[3], pool[3].astype(np.float64))  # never named: untouched
+
+
+# ---- the gate / beta projections (oracle.proj) --------------------------------------
+
+def _bits(x):
+    from oracle import proj
+    return proj.f64_to_bf16_bits(np.asarray(x, np.float64))
+
+
+def test_proj_round_bf16_against_brute_force():
+    """round_bf16 is the nearest bf16 value (ties to even), checked against a
+    search over every finite bf16 value near each input."""
+    from oracle import proj
+    rng = np.random.default_rng(3)
+    xs = np.concatenate([rng.standard_normal(300) * 10.0 ** rng.integers(-3, 4, 300),
+                         [257.0, 259.0, 1444.0, -257.0, 0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8]])
+    allbits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    allbits = allbits[(allbits & 0x7F80) != 0x7F80]   # drop infinities and NaNs
+    vals = proj.bf16_to_f64(allbits)
+    for x in xs:
+        d = np.abs(vals - x)
+        best = d.min()
+        cands = vals[d == best]
+        if len(cands) > 1:   # a tie: the candidate with an even last significand bit
+            cb = allbits[d == best]
+            cands = cands[(cb & 1) == 0]
+        assert proj.round_bf16(np.array([x]))[0] == cands[0], x
+
+
+def test_proj_hand_worked():
+    """One token, K = 8, hidden = 1..8; rows of w_ab and w_b chosen so every
+    value is worked out by hand:
+      P[0] = sum 1..8 = 36;  P[1] = 32 * 36 = 1152 (exact in bf16);
+      P[2] = 255 * 1 + 1 * 2 = 257 -> 256 (halfway between 256 and 258: even);
+      P[3] = 255 * 1 + 2 * 2 = 259 -> 260 (halfway between 258 and 260: even);
+      P[128] = 8 (last channel), P[129] = 1-2+3-4+5-6+7-8 = -4; other rows 0.
+      G[j] = P[j] for j < 4 (unit rows of w_b);
+      G[14] = P[3] - P[2] = 260 - 256 = 4;
+      G[15] = P[0] + P[1] + P[2] = 36 + 1152 + 256 = 1444 -> 1440 (bf16 spacing
+      8 at 2^10; 1444 is halfway between 1440 and 1448: even)."""
+    from oracle import proj
+    K = 8
+    hidden = np.arange(1, K + 1, dtype=np.float64)[None]
+    wab = np.zeros((130, K))
+    wab[0] = 1.0
+    wab[1] = 32.0
+    wab[2, 0], wab[2, 1] = 255.0, 1.0            # 257 is not a bf16 value: two terms
+    wab[3, 0], wab[3, 1] = 255.0, 2.0            # 255 + 4 = 259
+    wab[128, K - 1] = 1.0
+    wab[129] = [1, -1, 1, -1, 1, -1, 1, -1]
+    wb = np.zeros((16, 128))
+    for j in range(4):
+        wb[j, j] = 1.0
+    wb[14, 3], wb[14, 2] = 1.0, -1.0
+    wb[15, 0] = wb[15, 1] = wb[15, 2] = 1.0
+    p, g, p_exact, g_exact = proj.gate_proj(_bits(hidden), _bits(wab), _bits(wb))
+    want_p = np.zeros(130)
+    want_p[[0, 1, 2, 3, 128, 129]] = [36, 1152, 256, 260, 8, -4]
+    np.testing.assert_array_equal(p[0], want_p)
+    assert p_exact[0, 2] == 257 and p_exact[0, 3] == 259
+    want_g = np.zeros(16)
+    want_g[[0, 1, 2, 3, 14, 15]] = [36, 1152, 256, 260, 4, 1440]
+    np.testing.assert_array_equal(g[0], want_g)
+    assert g_exact[0, 15] == 1444
+
+
+def test_proj_brute_force_small_integers():
+    """Small integers (every sum exact in bf16) against plain Python loops."""
+    from oracle import proj
+    rng = np.random.default_rng(5)
+    M, K, nab, nb = 3, 16, 136, 32
+    h = rng.integers(-3, 4, (M, K)).astype(np.float64)
+    wab = rng.integers(-2, 3, (nab, K)).astype(np.float64)
+    wb = np.zeros((nb, 128))
+    wb[:, :6] = rng.integers(-1, 2, (nb, 6))
+    p, g, _, _ = proj.gate_proj(_bits(h), _bits(wab), _bits(wb))
+    for m in range(M):
+        for n in range(nab):
+            assert p[m, n] == sum(h[m, k] * wab[n, k] for k in range(K))
+        for n in range(nb):
+            assert g[m, n] == sum(p[m, j] * wb[n, j] for j in range(128))
