@@ -350,9 +350,9 @@ kda_status_t kda_gate_proj(const void* hidden, const void* w_ab, const void* w_b
   if (reinterpret_cast<uintptr_t>(g) % 2) return KDA_ERR_INVALID_ARG;
   const size_t need = kda_gate_proj_workspace_size(num_tokens, hidden_dim, n_ab);
   if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  if (num_tokens == 0) return KDA_OK;  // (needs no workspace)
   if (!workspace) return KDA_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(workspace) % 16) return KDA_ERR_INVALID_ARG;
-  if (num_tokens == 0) return KDA_OK;
 
   kda::ProjParams pp{};
   pp.hidden = static_cast<const uint16_t*>(hidden);

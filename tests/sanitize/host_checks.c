@@ -98,6 +98,25 @@ int main(void) {
                               FAKEI, FAKEI, 0, FAKEI, FAKE, FAKE, NULL, 8, 2, 2, KDA_STATE_FP32, wss),
          KDA_ERR_INVALID_ARG, "zero index stride");
 
+  // the gate / beta projections
+  const size_t wsp = kda_gate_proj_workspace_size(8, 7168, 144);
+  expect(wsp > 0, 1, "projection workspace size");
+  expect(kda_gate_proj_workspace_size(-1, 7168, 144) == 0, 1, "projection workspace, negative tokens");
+  expect(kda_gate_proj(NULL, FAKE, FAKE, FAKE, FAKE, FAKE, wsp, NULL, 8, 7168, 144, 1536),
+         KDA_ERR_INVALID_ARG, "projection, null hidden");
+  expect(kda_gate_proj(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wsp, NULL, 65537, 7168, 144, 1536),
+         KDA_ERR_INVALID_ARG, "projection, too many tokens");
+  expect(kda_gate_proj(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wsp, NULL, 8, 7170, 144, 1536),
+         KDA_ERR_INVALID_ARG, "projection, hidden_dim not a multiple of 8");
+  expect(kda_gate_proj(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wsp, NULL, 8, 7168, 120, 1536),
+         KDA_ERR_INVALID_ARG, "projection, n_ab below the rank");
+  expect(kda_gate_proj(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wsp, NULL, 8, 7168, 144, 1544),
+         KDA_ERR_INVALID_ARG, "projection, n_b not a multiple of 16");
+  expect(kda_gate_proj(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wsp - 1, NULL, 8, 7168, 144, 1536),
+         KDA_ERR_WORKSPACE_TOO_SMALL, "projection, short workspace");
+  expect(kda_gate_proj(NULL, FAKE, FAKE, NULL, NULL, NULL, 0, NULL, 0, 7168, 144, 1536), KDA_OK,
+         "projection of zero tokens");
+
   // status strings and the test hooks
   for (int c = -1; c <= 6; ++c) /* also values outside the enumerators */
     if (!kda_status_string((kda_status_t)c) || !strlen(kda_status_string((kda_status_t)c))) ++failures;
