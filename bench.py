@@ -58,17 +58,45 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def dominant_kernel(decode: bool, lower_bound: float) -> str:
-    """The kernel a call's time goes to (the library's automatic choice):
+def dominant_kernel(decode: bool, lower_bound: float, seg_len: int = 0, vs: int = 64) -> str:
+    """The kernels a call's time goes to (the library's automatic choice):
     the token-serial decode kernel for decode-sized calls, else the 16-token
-    pipelined kernel for lower_bound >= -5 and the 32-token one below."""
+    pipelined kernel for lower_bound >= -5 and the 32-token one below.  A call
+    that takes the segment-parallel schedule (seg_len > 0) runs four kernels,
+    named "+"-joined as rocprofv3 prints them (vs: the rerun's value slice)."""
     if decode:
         return "decode_kernel"
-    return "pipe_kernel" if lower_bound >= -5.0 else "fwd32_kernel"
+    if lower_bound < -5.0:
+        return "fwd32_kernel"
+    if seg_len:
+        return f"seg_plan_kernel+pipe_kernel<64, true>+seg_combine_kernel+pipe_kernel<{vs}, false>"
+    return "pipe_kernel"
+
+
+def plan_vsplit(heads: int, seqs: int, cus: int = 256) -> int:
+    """The library's value split (the pages' rule, doubled while it fits)."""
+    s = 1
+    while s < 8 and 2 * s * heads * seqs <= cus:
+        s *= 2
+    return s
+
+
+def call_kernels(args, T: int, H: int, N: int, lower_bound: float) -> str:
+    """dominant_kernel for a bench run's call, asking the library whether the
+    call takes the segment-parallel schedule."""
+    import gated_delta_rule_tok_amd as kda
+    decode = bool(args.decode_batch)
+    L = 0 if decode or args.checkpoint_interval else kda.kda_debug_segment_length(T, H, N)
+    vs = 64
+    if L:
+        s = args.vsplit or max(2, plan_vsplit(H, N + T // L))
+        vs = 128 // s
+    return dominant_kernel(decode, lower_bound, L, vs)
 
 
 def traffic_file(workload: str, kernel: str) -> str:
-    return os.path.join(PROFILES, f"traffic__{kernel}__{workload}.json")
+    label = kernel.replace("<", "").replace(">", "").replace(", ", "_")
+    return os.path.join(PROFILES, f"traffic__{label}__{workload}.json")
 
 
 def _pmc_sum(path: str, kernel_sub: str):
@@ -113,11 +141,13 @@ def traffic_from_pmc(pmc_dir: str, workload: str, command: str, kernel: str) -> 
 PROJ_KERNELS = "proj_ab_kernel+proj_out_kernel"
 
 
-def workload_name(args):
-    """(workload name, dominant kernel, the selecting arguments) of a run."""
+def workload_name(args, dims=None):
+    """(workload name, dominant kernel, the selecting arguments) of a run;
+    dims: the workload's (tokens, heads, sequences) if already known."""
     import kda_inputs as KI
     if getattr(args, "proj", 0):
         return f"proj_{args.proj}x7168_144_1536", PROJ_KERNELS, f"--proj {args.proj}"
+    apply_hooks(args)
     if args.decode_batch:
         wl, lb = f"decode_{args.decode_batch}x1_h16", KI.LOWER_BOUND
         sel = f"--decode-batch {args.decode_batch}"
@@ -128,7 +158,31 @@ def workload_name(args):
         lb = float(args.lower_bound)
         wl += f"_lb{args.lower_bound:g}"
         sel += f" --lower-bound {args.lower_bound:g}"
-    return wl, dominant_kernel(bool(args.decode_batch), lb), sel
+    if args.segments != "auto":
+        sel += f" --segments {args.segments}"
+    if args.vsplit:
+        sel += f" --vsplit {args.vsplit}"
+    if dims is not None:
+        T, H, N = dims
+    elif args.decode_batch:
+        T, H, N = args.decode_batch, 16, args.decode_batch
+    else:
+        c = KI.CONFIGS[args.config]
+        if c["lengths"] is None:
+            x = KI.config_inputs(args.config)
+            T, H, N = x.T, x.H, x.N
+        else:
+            T, H, N = sum(c["lengths"]), c["heads"], len(c["lengths"])
+    return wl, call_kernels(args, T, H, N, lb), sel
+
+
+def apply_hooks(args):
+    """The library's test hooks the run asks for: the segment schedule and
+    the value split."""
+    import gated_delta_rule_tok_amd as kda
+    seg = {"auto": 0, "off": 1}.get(args.segments)
+    kda.kda_debug_set_segment(int(args.segments) if seg is None else seg)
+    kda.kda_debug_set_vsplit(args.vsplit)
 
 
 PROJ_K, PROJ_NAB, PROJ_NB = 7168, 144, 1536
@@ -295,6 +349,11 @@ def main():
                     help="run the call this long before the warmup steps (clock ramp; 0: none)")
     ap.add_argument("--traffic-from", metavar="PMC_DIR",
                     help="write the traffic file for --config from rocprofv3 counter runs, then exit")
+    ap.add_argument("--segments", default="auto",
+                    help="the segment-parallel schedule for long sequences in calls with few "
+                         "(sequence, head) pairs: auto, off, or a segment length (multiple of 16)")
+    ap.add_argument("--vsplit", type=int, default=0,
+                    help="force the value split (1, 2, 4, 8); 0: the library's choice")
     ap.add_argument("--proj", type=int, default=0, metavar="M",
                     help="instead of the forward: time the gate / beta projections (kda_gate_proj) "
                          "for M tokens at hidden 7168, 144 = 128 + 16 rows, 1536 gate columns")
@@ -343,13 +402,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    apply_hooks(args)
     if args.decode_batch:
         x = KI.make_inputs([1] * args.decode_batch, 16, seed=7, init_state="fp32")
     else:
         x = KI.config_inputs(args.config)
     if args.lower_bound is not None:
         x.lower_bound = float(args.lower_bound)
-    x.meta["config"], kernel, _ = workload_name(args)
+    x.meta["config"], kernel, _ = workload_name(args, (x.T, x.H, x.N))
     T, H, N = x.T, x.H, x.N
     sbytes = 2 if x.state_bf16 else 4
     sdtype = torch.bfloat16 if x.state_bf16 else torch.float32

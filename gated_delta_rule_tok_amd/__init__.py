@@ -21,7 +21,7 @@ import os
 
 __all__ = ["kda_get_workspace_size", "kda_chunk_prefill_fwd", "kda_status_string",
            "kda_workspace_status",
-           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel", "kda_spec_decode_step", "kda_chunk_prefill_fwd_noalloc", "kda_gate_proj",
+           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel", "kda_debug_set_segment", "kda_debug_segment_length", "kda_spec_decode_step", "kda_chunk_prefill_fwd_noalloc", "kda_gate_proj",
            "kda_gate_proj_workspace_size", "KdaError", "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -106,6 +106,10 @@ def load_library():
         lib.kda_debug_set_kernel.restype = ctypes.c_int
         lib.kda_debug_set_vsplit.argtypes = [ctypes.c_int]
         lib.kda_debug_set_vsplit.restype = ctypes.c_int
+        lib.kda_debug_set_segment.argtypes = [ctypes.c_int]
+        lib.kda_debug_set_segment.restype = ctypes.c_int
+        lib.kda_debug_segment_length.argtypes = [I64, I32, I32]
+        lib.kda_debug_segment_length.restype = I32
         _lib = lib
     return _lib
 
@@ -147,6 +151,20 @@ def kda_debug_set_vsplit(s: int) -> int:
     if prev < 0:
         raise ValueError(f"invalid value split {s}")
     return prev
+
+
+def kda_debug_set_segment(length: int) -> int:
+    """Test hook: the segment-parallel schedule -- 0 automatic, 1 never, or
+    segments of `length` tokens (a multiple of 16) where the call allows it."""
+    prev = load_library().kda_debug_set_segment(int(length))
+    if prev < 0:
+        raise ValueError(f"invalid segment length {length}")
+    return prev
+
+
+def kda_debug_segment_length(num_tokens: int, heads: int, num_seqs: int) -> int:
+    """The segment length a call of these sizes would use (0: one piece)."""
+    return int(load_library().kda_debug_segment_length(int(num_tokens), int(heads), int(num_seqs)))
 
 
 def _check(t, name, dtype, shape=None, strided=False):

@@ -9,6 +9,7 @@
 // state dtype and the workspace capacity added so a C caller can be checked.
 // Failing fast on a bad configuration follows the same page's backend
 // resolver ("Implementation breakdown", item 1).
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -25,6 +26,7 @@ constexpr int kMaxDevices = 64;
 
 std::atomic<int> g_vsplit_override{0};
 std::atomic<int> g_kernel_override{0};
+std::atomic<int> g_segment_override{0};
 std::atomic<int> g_cu_count[kMaxDevices];
 
 thread_local char t_last_hip_error[256] = "";
@@ -104,14 +106,76 @@ int plan_vsplit(int heads, int seqs, int cus) {
   return s;
 }
 
+// ---- the segment-parallel schedule (kda_segment.hip) ---------------------------
+// Long sequences in a call with few (sequence, head) items are cut into
+// segments that run in parallel.  Taken when there are at most
+// kSegItemsMax items, at least kSegMinAvg tokens per sequence on average and
+// the workspace holds the segment area.  The segment length aims at about
+// kSegTarget / heads segments in the call (so summaries and reruns fill the
+// machine), at least kSegMinLen tokens, a multiple of 64 (whole rounds of
+// four 16-token chunks).
+constexpr int kSegItemsMax = 32;
+constexpr int64_t kSegMinAvg = 2048;
+constexpr int kSegTarget = 128;
+constexpr int kSegMinLen = 512;
+
+// Pseudo-sequences a call may use: a call that takes the schedule has at
+// most kSegItemsMax / heads sequences and kSegTarget / heads + its sequence
+// count segments, so pseudo-sequences x heads <= kSegSlots.
+constexpr int kSegSlots = kSegItemsMax + kSegTarget;
+int seg_cap(int heads) { return heads <= kSegItemsMax ? kSegSlots / heads : 0; }
+
+// The segment area, one size for every head count (so the workspace size
+// stays monotone): the table, first and count arrays for up to kSegSlots
+// pseudo-sequences, and kSegSlots (pseudo-sequence, head) slots of summaries
+// (local state, transition) and entering states, fp32 128 x 128 each.
+struct SegLayout {
+  size_t table, first, count, summ, starts, bytes;
+};
+constexpr size_t kDD = size_t(KDA_HEAD_DIM) * KDA_HEAD_DIM * sizeof(float);
+SegLayout seg_layout() {
+  SegLayout l{};
+  l.table = 0;
+  l.first = l.table + align_up(16 * size_t(kSegSlots));
+  l.count = l.first + align_up(4 * size_t(kSegSlots));
+  l.summ = l.count + align_up(4 * size_t(kSegSlots));
+  l.starts = l.summ + size_t(kSegSlots) * 2 * kDD;
+  l.bytes = l.starts + size_t(kSegSlots) * kDD;
+  return l;
+}
+
+// Status word and the sequence order table.
+size_t base_workspace_bytes(int32_t seqs) { return kAlign + align_up(sizeof(int32_t) * size_t(seqs)); }
+
+// Segment length of a call, or 0 for the plain schedule.  forced: the test
+// hook (0 automatic, 1 never, else that length).
+int plan_segment_len(int64_t T, int heads, int seqs, int forced) {
+  const int cap = seg_cap(heads);
+  if (forced == 1 || cap == 0 || T == 0) return 0;
+  int64_t L;
+  if (forced > 1) {
+    L = forced;
+  } else {
+    if (int64_t(seqs) * heads > kSegItemsMax || T < kSegMinAvg * seqs) return 0;
+    const int64_t target = kSegTarget / heads;
+    L = (T + target - 1) / target;
+    L = std::max<int64_t>(kSegMinLen, (L + 63) / 64 * 64);
+  }
+  if (seqs + T / L > cap) return 0;
+  return int(L);
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t kda_get_workspace_size(int64_t max_tokens, int32_t heads, int32_t max_seqs) {
   if (max_tokens < 0 || heads <= 0 || max_seqs <= 0) return 0;
-  // status word (padded to kAlign), then the sequence order table (longest first)
-  return kAlign + align_up(sizeof(int32_t) * size_t(max_seqs));
+  // status word (padded to kAlign), the sequence order table (longest first),
+  // and, where some call within these bounds may take the segment-parallel
+  // schedule, its area (independent of the token and sequence counts)
+  const size_t seg = max_tokens >= kSegMinAvg ? seg_layout().bytes : 0;
+  return base_workspace_bytes(max_seqs) + seg;
 }
 
 const char* kda_status_string(kda_status_t status) {
@@ -132,6 +196,17 @@ int kda_debug_set_kernel(int k) {
   // staging (4 tokens), 4 pipelined 16-token, 5 pipelined 32-token
   if (k < 0 || k > 5) return -1;
   return g_kernel_override.exchange(k);
+}
+
+int kda_debug_set_segment(int len) {
+  // 0 automatic, 1 never, else force segments of len tokens (a multiple of 16)
+  if (!(len == 0 || len == 1 || (len >= 16 && len % 16 == 0 && len <= (1 << 24)))) return -1;
+  return g_segment_override.exchange(len);
+}
+
+int32_t kda_debug_segment_length(int64_t num_tokens, int32_t heads, int32_t num_seqs) {
+  if (num_tokens < 0 || heads <= 0 || num_seqs <= 0) return 0;
+  return plan_segment_len(num_tokens, heads, num_seqs, g_segment_override.load(std::memory_order_relaxed));
 }
 
 int kda_debug_set_vsplit(int s) {
@@ -208,9 +283,10 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
     if (!fixed_status) return KDA_ERR_INVALID_ARG;
     if (num_seqs > kNoAllocMaxSeqs) return KDA_ERR_INVALID_ARG;
   } else {
-    const size_t need = kda_get_workspace_size(num_tokens, heads, num_seqs);
+    // the segment area is optional: without it the call takes the plain schedule
+    const size_t need = base_workspace_bytes(num_seqs);
     if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
-    if (need > 0 && !workspace) return KDA_ERR_INVALID_ARG;
+    if (!workspace) return KDA_ERR_INVALID_ARG;
   }
 
   // ---- plan --------------------------------------------------------------------
@@ -287,6 +363,58 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   if ((kernel == 4 || kernel == 5) && p.vsplit == 1 && forced == 0) p.vsplit = 2;
   if (kernel == 4 && p.vsplit == 1) kernel = 1;
   if (checkpoints && kernel != 4 && kernel != 5) return KDA_ERR_UNSUPPORTED;
+
+  // segment-parallel schedule: summaries, combine, rerun (kda_segment.hip)
+  if (kernel == 4 && !checkpoints && !sp_idx && !fixed_scratch &&
+      reinterpret_cast<uintptr_t>(workspace) % 16 == 0) {
+    const int L = plan_segment_len(num_tokens, heads, num_seqs,
+                                   g_segment_override.load(std::memory_order_relaxed));
+    const SegLayout lay = seg_layout();
+    const size_t off = base_workspace_bytes(num_seqs);
+    if (L > 0 && workspace_bytes >= off + lay.bytes) {
+      char* w = static_cast<char*>(workspace) + off;
+      kda::SegParams sp{};
+      sp.cu = cu_seqlens;
+      sp.N = num_seqs;
+      sp.T = int(num_tokens);
+      sp.H = heads;
+      sp.L = L;
+      sp.M = num_seqs + int(num_tokens / L);
+      sp.table = reinterpret_cast<int32_t*>(w + lay.table);
+      sp.first = reinterpret_cast<int32_t*>(w + lay.first);
+      sp.count = reinterpret_cast<int32_t*>(w + lay.count);
+      sp.s0 = initial_state;
+      sp.s0_bf16 = sdt == KDA_STATE_BF16;
+      sp.summ = reinterpret_cast<const float*>(w + lay.summ);
+      sp.starts = reinterpret_cast<float*>(w + lay.starts);
+      if (hipError_t e = kda::launch_seg_plan(sp, st); e != hipSuccess)
+        return hip_failure(e, "segment plan launch");
+      kda::Params pa = p;  // summaries: [local state | transition], 4 slices of 64
+      pa.seg = sp.table;
+      pa.seg_mode = 1;
+      pa.N = sp.M;
+      pa.vsplit = 4;
+      pa.order = nullptr;
+      pa.s0 = nullptr;
+      pa.sT = const_cast<float*>(sp.summ);
+      pa.state_bf16 = 0;
+      if (hipError_t e = kda::launch_pipe(pa, st); e != hipSuccess)
+        return hip_failure(e, "segment summary launch");
+      if (hipError_t e = kda::launch_seg_combine(sp, st); e != hipSuccess)
+        return hip_failure(e, "segment combine launch");
+      kda::Params pc = p;  // rerun of every segment from its entering state
+      pc.seg = sp.table;
+      pc.seg_mode = 2;
+      pc.N = sp.M;
+      pc.vsplit = forced > 0 ? forced : std::max(2, plan_vsplit(heads, sp.M, cus));
+      pc.order = nullptr;
+      pc.s0 = sp.starts;
+      if (hipError_t e = kda::launch_pipe(pc, st); e != hipSuccess)
+        return hip_failure(e, "segment rerun launch");
+      return KDA_OK;
+    }
+  }
+
   // the sequence order table (longest first): the pipelined kernels rank a
   // few sequences themselves, the decode path takes them in index order, the
   // others read the table

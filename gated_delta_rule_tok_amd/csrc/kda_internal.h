@@ -56,7 +56,41 @@ struct Params {
   const int32_t* sp_acc;
   int sp_stride;
   int64_t sp_slots;
+  // segment-parallel schedule (pipelined 16-token kernel only): null, or one
+  // entry of four ints per pseudo-sequence m = 0 .. N - 1 of the grid (N is
+  // then the entry count): the sequence n (-1: unused entry, the workgroup
+  // exits), its first and end token, flags (bit 0: n's last segment).
+  //   seg_mode 1, summaries: the slices cover 256 columns, the local state
+  //     (values v, from zero) and the transition (values 0, from the
+  //     identity); outputs are not written; both go to sT = [N, H, 2, D, D]
+  //     fp32 at m.  Last segments have no summary (they exit).
+  //   seg_mode 2, rerun: the initial state is s0 = [N, H, D, D] fp32 at m;
+  //     the final state goes to sT at sequence n, in the state dtype, for
+  //     last segments only.
+  const int32_t* seg;
+  int seg_mode;
 };
+
+// Pseudo-sequences of the segment-parallel schedule (kda_segment.hip).  Each
+// sequence n is cut into count[n] = max(1, ceil(len / L)) segments of L tokens
+// (the last shorter), pseudo-sequences first[n] .. first[n] + count[n] - 1.
+struct SegParams {
+  const int32_t* cu;  // [N + 1] sequence offsets (clamped like the kernels do)
+  int N, T, H, L;
+  int M;              // table entries (the grid's pseudo-sequences), >= N + T / L
+  int32_t* table;     // [M][4]: n (or -1), first token, end token, flags (bit 0: last)
+  int32_t* first;     // [N]
+  int32_t* count;     // [N]
+  const void* s0;     // the caller's initial state [N, H, D, D] (null: zeros)
+  int s0_bf16;
+  const float* summ;  // [M, H, 2, D, D]: local state, transition
+  float* starts;      // [M, H, D, D]: the state entering each pseudo-sequence
+};
+// The table (one workgroup).
+hipError_t launch_seg_plan(const SegParams& sp, hipStream_t stream);
+// The states entering every segment: S_0 = the initial state, S_{j+1} =
+// P_j S_j + R_j in fp32, one workgroup per (sequence, head, 16 columns).
+hipError_t launch_seg_combine(const SegParams& sp, hipStream_t stream);
 
 // ---- bf16 helpers (bf16 is the high half of an IEEE fp32) -------------------
 

@@ -530,7 +530,10 @@ struct Smem {
   Sync sy;
 };
 
-template <int VS>
+// SUMM: the summary step of the segment-parallel schedule (p.seg_mode 1;
+// see Params::seg): slices over 256 columns, the transition half with zero
+// values from the identity, no outputs.
+template <int VS, bool SUMM>
 __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   using C = Cfg<VS>;
   constexpr int SPW = C::SPW, NSW = C::NSW;
@@ -553,8 +556,16 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   // sequence of rank rest / H (longest first, ties by index): from the plan
   // table, or ranked here when there are few sequences
   if (tid < int(sizeof(Sync) / sizeof(int))) reinterpret_cast<int*>(&sm.sy)[tid] = 0;
-  int n;
-  if (p.order) {
+  int n, m = 0;  // sequence; pseudo-sequence (segment) of the segment-parallel schedule
+  int4 segent = {0, 0, 0, 1};
+  if (p.seg) {
+    m = rest / H;
+    segent = reinterpret_cast<const int4*>(p.seg)[m];
+    n = __builtin_amdgcn_readfirstlane(segent.x);
+    // unused entries, and last segments in the summary step, have nothing to
+    // do (the whole workgroup leaves: n and the flags are uniform)
+    if (n < 0 || (SUMM && (__builtin_amdgcn_readfirstlane(segent.w) & 1))) return;
+  } else if (p.order) {
     n = p.order[rest / H];
   } else {
     // scratch in a package that nothing uses yet (no other LDS allocation, so
@@ -582,8 +593,9 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
 
   // the bounds are uniform: scalar registers (else every buffer access with a
   // token offset in its scalar operand becomes a loop over lanes)
-  const int bos = __builtin_amdgcn_readfirstlane(min(max(p.cu[n], 0), p.T));
-  const int eos = __builtin_amdgcn_readfirstlane(min(max(p.cu[n + 1], bos), p.T));
+  const int bos = __builtin_amdgcn_readfirstlane(min(max(p.seg ? segent.y : p.cu[n], 0), p.T));
+  const int eos = __builtin_amdgcn_readfirstlane(min(max(p.seg ? segent.z : p.cu[n + 1], bos), p.T));
+  const bool seg_last = (__builtin_amdgcn_readfirstlane(segent.w) & 1) != 0;
   const int nc = (eos - bos + kTok - 1) / kTok;  // chunks
   const int nr = (nc + kPW - 1) / kPW;            // rounds
 
@@ -648,10 +660,19 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   __builtin_amdgcn_s_setprio(2);
   // S[u][rt][j] = S[16 rt + 4 g4 + j][column of strip u]
   const int sw = wave - kProdWaves;
-  const int colb = slice * VS + 16 * sw + l16;  // column of strip 0; strip u adds 16 NSW u
-  const __amdgpu_buffer_rsrc_t vsrc = rows_rsrc(p.v + size_t(h) * p.hs_v, eos, p.ts_v, kD);
+  // summary step: slices 0 .. vsplit/2 - 1 carry the local state, the others
+  // the transition, whose values are zero (an empty range: its loads read
+  // zeros without touching memory)
+  const bool trans = SUMM && slice >= p.vsplit / 2;
+  const int vslice = trans ? slice - p.vsplit / 2 : slice;
+  const int colb = vslice * VS + 16 * sw + l16;  // column of strip 0; strip u adds 16 NSW u
+  const __amdgpu_buffer_rsrc_t vsrc = rows_rsrc(p.v + size_t(h) * p.hs_v, trans ? 0 : eos, p.ts_v, kD);
   const __amdgpu_buffer_rsrc_t odst = rows_rsrc(p.out + size_t(h) * p.hs_o, eos, p.ts_o, kD);
+  // the state's [D, D] block: sequence n's, or in the segment-parallel
+  // schedule the segment's (summary: local state, then transition)
   const size_t sbase = (size_t(n) * H + h) * kD * kD;
+  const size_t segbase = SUMM ? ((size_t(m) * H + h) * 2 + (trans ? 1 : 0)) * kD * kD
+                              : (size_t(m) * H + h) * kD * kD;
   f32x4 S[SPW][8];
   // this wave's strips of the state, in the state dtype, into the [D, D]
   // block at dst + base
@@ -693,11 +714,29 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
     ck_chunks = p.ck_int / kTok;
     ck_next = ck_chunks;
   }
-  if (!p.s0) {
+  if (SUMM) {
+    // local state from zero, transition from the identity
+#pragma unroll
+    for (int u = 0; u < SPW; ++u)
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          S[u][rt][j] = trans && 16 * rt + 4 * g4 + j == colb + 16 * NSW * u ? 1.f : 0.f;
+  } else if (!p.s0) {
 #pragma unroll
     for (int u = 0; u < SPW; ++u)
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt) S[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else if (p.seg) {
+    // a segment's entering state (fp32, from the combine step)
+    const float* s0 = static_cast<const float*>(p.s0) + segbase + colb;
+#pragma unroll
+    for (int u = 0; u < SPW; ++u)
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[u][rt][j] = s0[(16 * rt + 4 * g4 + j) * kD + 16 * NSW * u];
   } else if (p.state_bf16) {
     const uint16_t* s0 = static_cast<const uint16_t*>(p.s0) + sbase + colb;
     uint16_t raw0[SPW][8][4];
@@ -725,7 +764,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
   // values of each round's chunks, loaded one round before use into two
   // alternating register sets (no copies, so nothing waits for the output
   // stores issued in between)
-  const unsigned cstrip = unsigned(slice * VS + 16 * sw);  // first column of strip 0
+  const unsigned cstrip = unsigned(vslice * VS + 16 * sw);  // first column of strip 0
   uint2 va[kPW][SPW], vbuf[kPW][SPW];
 #pragma unroll
   for (int c = 0; c < kPW; ++c)
@@ -811,17 +850,19 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
         Tiles& tl = sm.t[sw][u];
         const f32x4 D = V[u] - Y;
         const f32x4 N = mfma16(Lf, to_bf16x4(D), bR * D);
-        const f32x4 O = mfma16(Mf, to_bf16x4(N), rqR * Q);
-        // O into rows: written column-major, read back transposed (lane l16
-        // of group g4: columns 4 g4 .. + 3 of token l16), one 8-byte store
-        // per lane; rows past the sequence end are dropped by the range check
-        *reinterpret_cast<uint2*>(&tl.o[16 * l16 + 4 * g4]) = uint2{pk2(O[0], O[1]), pk2(O[2], O[3])};
-        __builtin_amdgcn_wave_barrier();
-        const bf16x4 orow = tr4(&tl.o[64 * g4 + 16 * (l16 >> 2) + 4 * (l16 & 3)]);
-        __builtin_amdgcn_raw_buffer_store_b64(
-            __builtin_bit_cast(u32x2, orow), odst,
-            ((unsigned(t0) + unsigned(l16)) * unsigned(p.ts_o) + cstrip + 16 * NSW * u + 4u * g4) * 2u,
-            0, 0);
+        if constexpr (!SUMM) {  // (the summary step writes no output)
+          const f32x4 O = mfma16(Mf, to_bf16x4(N), rqR * Q);
+          // O into rows: written column-major, read back transposed (lane l16
+          // of group g4: columns 4 g4 .. + 3 of token l16), one 8-byte store
+          // per lane; rows past the sequence end are dropped by the range check
+          *reinterpret_cast<uint2*>(&tl.o[16 * l16 + 4 * g4]) = uint2{pk2(O[0], O[1]), pk2(O[2], O[3])};
+          __builtin_amdgcn_wave_barrier();
+          const bf16x4 orow = tr4(&tl.o[64 * g4 + 16 * (l16 >> 2) + 4 * (l16 & 3)]);
+          __builtin_amdgcn_raw_buffer_store_b64(
+              __builtin_bit_cast(u32x2, orow), odst,
+              ((unsigned(t0) + unsigned(l16)) * unsigned(p.ts_o) + cstrip + 16 * NSW * u + 4u * g4) * 2u,
+              0, 0);
+        }
         // S <- (Diag(e^{G_last}) S) + K'^T N in fp16 operands (kKpScale K' and
         // kNScale N; k-slots: this lane group's four tokens).  The accumulator
         // comes from the VALU (the decay above), never straight from a product
@@ -857,7 +898,10 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
     }
   }
 
-  store_state(p.sT, sbase);  // final state
+  // final state: the sequence's (or, in the segment-parallel schedule, its
+  // last segment's), or the summary of a segment
+  if (SUMM) store_state(p.sT, segbase);
+  else if (seg_last) store_state(p.sT, sbase);
   if (lane == 0 && gave_up(&sm.sy.err)) p.errword[0] = 1;
 }
 
@@ -866,11 +910,17 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
 hipError_t launch_pipe(const Params& p, hipStream_t stream) {
   const void* fn = nullptr;
   int threads = 0;
-  switch (kD / p.vsplit) {
-    case 64: fn = reinterpret_cast<const void*>(&pipe_kernel<64>); threads = Cfg<64>::kThreads; break;
-    case 32: fn = reinterpret_cast<const void*>(&pipe_kernel<32>); threads = Cfg<32>::kThreads; break;
-    case 16: fn = reinterpret_cast<const void*>(&pipe_kernel<16>); threads = Cfg<16>::kThreads; break;
-    default: return hipErrorInvalidValue;
+  if (p.seg_mode == 1) {  // summaries: 4 slices of 64 over 256 columns
+    if (p.vsplit != 4 || !p.seg) return hipErrorInvalidValue;
+    fn = reinterpret_cast<const void*>(&pipe_kernel<64, true>);
+    threads = Cfg<64>::kThreads;
+  } else {
+    switch (kD / p.vsplit) {
+      case 64: fn = reinterpret_cast<const void*>(&pipe_kernel<64, false>); threads = Cfg<64>::kThreads; break;
+      case 32: fn = reinterpret_cast<const void*>(&pipe_kernel<32, false>); threads = Cfg<32>::kThreads; break;
+      case 16: fn = reinterpret_cast<const void*>(&pipe_kernel<16, false>); threads = Cfg<16>::kThreads; break;
+      default: return hipErrorInvalidValue;
+    }
   }
   Params arg = p;
   void* args[] = {&arg};

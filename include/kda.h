@@ -81,6 +81,16 @@ typedef enum { KDA_STATE_FP32 = 0, KDA_STATE_BF16 = 1 } kda_state_dtype_t;
  * wrapper listing makes once at construction with max_num_batched_tokens,
  * local_num_heads, max_num_seqs).  Pure, host-only, monotone in every
  * argument.  Returns 0 for negative or zero-sized arguments.
+ *
+ * The size has two parts.  A call needs the first (the status word and a
+ * sequence order table, 4 bytes per sequence); with less it returns
+ * KDA_ERR_WORKSPACE_TOO_SMALL.  The second (31.5 MB when max_tokens >= 2048,
+ * else none) holds the segment-parallel schedule: long
+ * sequences in a call with at most 32 (sequence, head) pairs are cut into
+ * segments that run at once (each segment's state map P S + R, then the
+ * states entering the segments, then every segment from its state).  A call
+ * given only the first part runs every sequence in one piece; results agree
+ * within the tolerances, not bit for bit.
  */
 size_t kda_get_workspace_size(int64_t max_tokens, int32_t heads, int32_t max_seqs);
 
@@ -362,6 +372,27 @@ const char* kda_last_hip_error(void);
  * unchanged) for an invalid value.
  */
 int kda_debug_set_vsplit(int s);
+
+/*
+ * Test hook: the segment-parallel schedule -- 0 (default): automatic (at most
+ * 32 (sequence, head) pairs and at least 2048 tokens per sequence on average,
+ * segments of about 128 / heads per call, at least 512 tokens); 1: never;
+ * a multiple of 16 from 16 to 2^24: segments of that many tokens whenever
+ * the pipelined 16-token kernel runs the call, heads <= 32 and the segment
+ * area holds them ((sequences + num_tokens / len) * heads <= 160).
+ * Process-wide.  Returns
+ * the previous setting, or -1 (setting unchanged) for an invalid value.
+ */
+int kda_debug_set_segment(int len);
+
+/*
+ * Diagnostic: the segment length the segment-parallel schedule would use for a
+ * call of these sizes on the pipelined 16-token kernel with a workspace of
+ * kda_get_workspace_size bytes (under the current kda_debug_set_segment
+ * setting), or 0 when such a call runs every sequence in one piece.  Host
+ * only, no HIP call.
+ */
+int32_t kda_debug_segment_length(int64_t num_tokens, int32_t heads, int32_t num_seqs);
 
 /*
  * Test hook: choose the kernel family -- 0 (default): automatic.  A call

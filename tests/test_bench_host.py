@@ -56,3 +56,26 @@ def test_dominant_kernel_follows_the_library_choice():
     assert bench.dominant_kernel(False, -5.0) == "pipe_kernel"
     assert bench.dominant_kernel(False, -1.0) == "pipe_kernel"
     assert bench.dominant_kernel(False, -5.25) == "fwd32_kernel"
+    seg = bench.dominant_kernel(False, -5.0, 2048, 64)
+    assert seg.split("+") == ["seg_plan_kernel", "pipe_kernel<64, true>", "seg_combine_kernel",
+                              "pipe_kernel<64, false>"]
+    assert bench.traffic_file("w", seg).endswith(
+        "traffic__seg_plan_kernel+pipe_kernel64_true+seg_combine_kernel+pipe_kernel64_false__w.json")
+
+
+def test_bench_labels_the_segmented_workloads():
+    """configs 2 and 3 (one or two long sequences, few heads) take the
+    segment-parallel schedule; config 1 does not; --segments off turns it off."""
+    import argparse
+    import bench
+    a = argparse.Namespace(proj=0, decode_batch=0, config=2, lower_bound=None, segments="auto",
+                           vsplit=0, checkpoint_interval=0)
+    assert bench.workload_name(a)[1].startswith("seg_plan_kernel+")
+    a.config = 3
+    assert bench.workload_name(a)[1].startswith("seg_plan_kernel+")
+    a.config = 1
+    assert bench.workload_name(a)[1] == "pipe_kernel"
+    a.config, a.segments = 2, "off"
+    assert bench.workload_name(a)[1] == "pipe_kernel"
+    a.segments = "auto"
+    bench.apply_hooks(a)

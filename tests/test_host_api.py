@@ -34,6 +34,7 @@ def test_library_exports_every_declared_symbol():
                           "kda_chunk_prefill_fwd_strided", "kda_chunk_prefill_fwd_checkpoints",
                           "kda_status_string",
                           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel",
+                          "kda_debug_set_segment", "kda_debug_segment_length",
                           "kda_spec_decode_step", "kda_chunk_prefill_fwd_noalloc",
                           "kda_gate_proj", "kda_gate_proj_workspace_size"}
     for n in names:
@@ -117,10 +118,67 @@ def test_lower_bound_outside_range_unsupported(lb):
 def test_workspace_too_small():
     need = kda.kda_get_workspace_size(16384, 16, 8)
     assert need > 0
-    assert _call(wsb=need - 1) == WS_SMALL
+    # a call needs the status word and the order table; the segment area is optional
+    base = 256 + 256
+    assert _call(wsb=base - 1) == WS_SMALL
     assert _call(wsb=0) == WS_SMALL
     # enough bytes claimed but no pointer
     assert _call(ws=None, wsb=need) == INVALID
+    assert _call(ws=None, wsb=base) == INVALID
+
+
+# The segment area: 160 table entries (16 bytes), first/count ints, and 160
+# (pseudo-sequence, head) slots of a summary (local state and transition) and
+# an entering state, fp32 128 x 128 each; the same for every head count.
+SEG_AREA = 2560 + 768 + 768 + 160 * 3 * 128 * 128 * 4
+
+
+@pytest.mark.parametrize("heads", [1, 2, 3, 4, 16, 32, 33, 64])
+def test_workspace_segment_area(heads):
+    f = kda.kda_get_workspace_size
+    base = 256 + 256
+    assert f(2047, heads, 8) == base                    # no call this small segments
+    assert f(2048, heads, 8) == base + SEG_AREA
+    assert f(1 << 20, heads, 1) == 256 + 256 + SEG_AREA  # independent of the token count
+    assert SEG_AREA < 32 << 20
+
+
+@pytest.mark.parametrize("T,H,N,L", [
+    (16384, 16, 1, 2048),    # 1 x 16384, 16 heads: 128 / 16 = 8 segments
+    (16384, 4, 2, 512),      # 2 x 8192, 4 heads: 32 segments of 512
+    (8192, 4, 1, 512),       # at least 512 tokens
+    (16384, 16, 8, 0),       # 128 (sequence, head) pairs: one piece
+    (256, 2, 1, 0),          # fewer than 2048 tokens per sequence
+    (65536, 32, 1, 16384),   # 128 / 32 = 4 segments; 1 + 4 pseudo-sequences x 32 <= 160
+    (4096, 32, 1, 1024),     # the same cut at 4096 tokens
+    (65536, 32, 2, 0),       # 64 (sequence, head) pairs: one piece
+    (0, 4, 1, 0),
+])
+def test_segment_plan(T, H, N, L):
+    assert kda.kda_debug_segment_length(T, H, N) == L
+
+
+def test_segment_plan_follows_the_hook():
+    prev = kda.kda_debug_set_segment(1)
+    try:
+        assert kda.kda_debug_segment_length(16384, 16, 1) == 0
+        kda.kda_debug_set_segment(64)
+        assert kda.kda_debug_segment_length(2000, 2, 3) == 64    # 3 + 31 = 34 <= 80
+        assert kda.kda_debug_segment_length(6000, 2, 3) == 0     # 3 + 93 > 80
+        assert kda.kda_debug_segment_length(16384, 16, 8) == 0   # 8 + 256 > 10
+    finally:
+        kda.kda_debug_set_segment(prev)
+
+
+def test_debug_segment_hook():
+    lib = kda.load_library()
+    for bad in (-1, 2, 15, 24, 1 << 25):
+        assert lib.kda_debug_set_segment(bad) == -1
+    prev = lib.kda_debug_set_segment(64)
+    assert lib.kda_debug_set_segment(1) == 64
+    assert lib.kda_debug_set_segment(prev) == 1
+    with pytest.raises(ValueError):
+        kda.kda_debug_set_segment(17)
 
 
 def test_python_binding_rejects_cpu_tensors():
