@@ -287,8 +287,9 @@ __device__ __forceinline__ float chan(uint2 w, int i) {
 // decayed operand of the half's 64 channels.  Writes X = e^G k~ and Q_T =
 // e^G q, the products' right operand K_G = e^{-G} k~ (to `kg`), kKpScale K'
 // (fp16), gam, and rqs (second half) or beta (first half).  FULL: all 16
-// tokens are inside the sequence (no masking).
-template <bool FULL>
+// tokens are inside the sequence (no masking).  NOQ: no output is formed
+// (the summary step), so neither Q_T nor rqs.
+template <bool FULL, bool NOQ = false>
 __device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, Raw& raw,
                                                  const RawLoad& ld, int tn, int hf, int Lc, int lane,
                                                  const float* c2, float c1, float lb2, float scale) {
@@ -319,8 +320,10 @@ __device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, Raw& raw,
     const float sk = row_norm2(raw.kn);
     if ((lane & 3) == 0) pk.rk[hf][lane >> 2] = rsqrtf(sk + kNormEps);
     if (hf) {
-      const float sq = row_norm2(raw.qn);
-      if ((lane & 3) == 0) pk.rqs[lane >> 2] = rsqrtf(sq + kNormEps) * scale;
+      if constexpr (!NOQ) {
+        const float sq = row_norm2(raw.qn);
+        if ((lane & 3) == 0) pk.rqs[lane >> 2] = rsqrtf(sq + kNormEps) * scale;
+      }
     } else if (lane < kTok) {
       pk.beta[lane] = lane < Lc ? rcp(1.f + ex2(-kLog2e * bf16_to_f32(uint16_t(raw.beta)))) : 0.f;
     }
@@ -364,14 +367,13 @@ __device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, Raw& raw,
       const float G = fmaf(cs[i][rr], lb2, off[i]);
       const float E = ex2(G), F = ex2(-G);
       const float kv = chan(raw.k[rr], i) * rk4[rr];
-      const float qv = chan(raw.q[rr], i);
       vx[rr] = kv * E;
-      vq[rr] = qv * E;
+      if constexpr (!NOQ) vq[rr] = chan(raw.q[rr], i) * E;
       vg[rr] = kv * F;
       vk[rr] = vg[rr] * g16;
     }
     *reinterpret_cast<uint2*>(&pk.x[row]) = uint2{pk2(vx[0], vx[1]), pk2(vx[2], vx[3])};
-    *reinterpret_cast<uint2*>(&pk.qt[row]) = uint2{pk2(vq[0], vq[1]), pk2(vq[2], vq[3])};
+    if constexpr (!NOQ) *reinterpret_cast<uint2*>(&pk.qt[row]) = uint2{pk2(vq[0], vq[1]), pk2(vq[2], vq[3])};
     *reinterpret_cast<uint2*>(&kg[row]) = uint2{pk2(vg[0], vg[1]), pk2(vg[2], vg[3])};
     *reinterpret_cast<uint2*>(&pk.kp[fragx(c >> 4, c & 15, 4 * tq)]) =
         uint2{pk2h(vk[0], vk[1]), pk2h(vk[2], vk[3])};
@@ -608,10 +610,11 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
     constexpr int hf = decltype(half)::value;
     const int c = wave & (kPW - 1);
     RawSrc src;
-    src.q = rows_rsrc(p.q + size_t(h) * p.hs_q, eos, p.ts_q, kD);
+    // (the summary step forms no output: no q, its loads read zeros)
+    src.q = rows_rsrc(p.q + size_t(h) * p.hs_q, SUMM ? 0 : eos, p.ts_q, kD);
     src.k = rows_rsrc(p.k + size_t(h) * p.hs_k, eos, p.ts_k, kD);
     src.g = rows_rsrc(p.g + size_t(h) * p.hs_g, eos, p.ts_g, kD);
-    src.qn = rows_rsrc(p.q + size_t(h) * p.hs_q, hf ? eos : 0, p.ts_q, kD);
+    src.qn = rows_rsrc(p.q + size_t(h) * p.hs_q, hf && !SUMM ? eos : 0, p.ts_q, kD);
     src.beta = rows_rsrc(p.beta + size_t(h) * p.hs_b, hf ? 0 : eos, p.ts_b, 1);
     const float eA = expf(p.A_log[h]);
     const float c1 = -kLog2e * eA;
@@ -638,12 +641,12 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
       // one code path for full and partial chunks: with two, the registers
       // of the next chunk's loads differ between them and the merge copies
       // them, which waits for the loads at the end of every round
-      produce_operands<false>(P, kg, raw, ld, tn, hf, Lc, lane, c2, c1, lb2, p.scale);
+      produce_operands<false, SUMM>(P, kg, raw, ld, tn, hf, Lc, lane, c2, c1, lb2, p.scale);
       // both halves' operands (the products run over all 128 channels)
       arrive(&sm.sy.half[c], lane);
       wait_count(&sm.sy.half[c], kPH * (r + 1), &sm.sy.err);
       if (hf == 0) produce_inverse(P, kg, lane);
-      else produce_m(P, kg, lane);
+      else if (!SUMM) produce_m(P, kg, lane);
       arrive(&sm.sy.rdy[r & 1][c], lane);
     }
   };
@@ -805,7 +808,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
         const int r1 = 32 * kb2 + 4 * g4 + (l16 >> 2), r2 = r1 + 16;
         const int o1 = swz(r1) * kTok + col, o2 = swz(r2) * kTok + col;
         ax[kb2] = cat(tr4(&P.x[o1]), tr4(&P.x[o2]));
-        aq[kb2] = cat(tr4(&P.qt[o1]), tr4(&P.qt[o2]));
+        if constexpr (!SUMM) aq[kb2] = cat(tr4(&P.qt[o1]), tr4(&P.qt[o2]));
       }
       const f32x4 bR = *reinterpret_cast<const f32x4*>(&P.beta[4 * g4]);
       const f32x4 rqR = *reinterpret_cast<const f32x4*>(&P.rqs[4 * g4]);
@@ -834,7 +837,7 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
 #pragma unroll
         for (int kb2 = 0; kb2 < 4; ++kb2) {
           Y = mfma32(ax[kb2], Sb[kb2], Y);
-          Q = mfma32(aq[kb2], Sb[kb2], Q);
+          if constexpr (!SUMM) Q = mfma32(aq[kb2], Sb[kb2], Q);  // (output only)
         }
         // the products are issued here; the decay Diag(e^{G_last}) of the
         // state (its bf16 copy is already taken) is applied while they run,
