@@ -218,10 +218,12 @@ kda_status_t kda_chunk_prefill_fwd_strided(
  *
  * Every other argument, limit and guarantee is that of the forward call.
  * The work runs on a pipelined kernel whatever the call's size (the 16-token
- * one for lower_bound >= -5, the 32-token one below), so out and final_state
- * are bit for bit those of the forward call except for decode-sized calls (at
- * most 8 tokens per sequence on average), where the forward call takes the
- * token-serial decode kernel (both within the tolerances of the oracle).
+ * one for lower_bound >= -5, the 32-token one below), always in one piece per
+ * sequence (no segment-parallel schedule), so out and final_state are bit for
+ * bit those of the forward call given a workspace without the segment area;
+ * the forward call differs from them (within the tolerances of the oracle)
+ * where it takes the token-serial decode kernel (decode-sized calls, at most
+ * 8 tokens per sequence on average) or the segment-parallel schedule.
  * Returns KDA_ERR_INVALID_ARG for a NULL checkpoints, a bad interval or a
  * short capacity, and KDA_ERR_UNSUPPORTED under a kda_debug_set_kernel /
  * kda_debug_set_vsplit override that selects a kernel other than the
@@ -254,7 +256,9 @@ kda_status_t kda_chunk_prefill_fwd_checkpoints(
  * calls that may overlap on one device (different streams without ordering
  * between them) race on it and give undefined results.  Every other argument,
  * limit and guarantee is that of kda_chunk_prefill_fwd on dense tensors, with
- * the same results bit for bit.
+ * the same results bit for bit as a call given a workspace without the
+ * segment area (there is no room for the segment-parallel schedule here, so
+ * every sequence runs in one piece).
  */
 kda_status_t kda_chunk_prefill_fwd_noalloc(
     const void* q, const void* k, const void* v, const void* g, const void* beta_logits,

@@ -214,3 +214,26 @@ def test_segments_weak_decay(lb):
     torch.cuda.synchronize()
     oref, fref = run_oracle(x)
     assert_parity(x, out, fin, oref, fref, label=f"segments, lower_bound {lb}", relative=True)
+
+
+def test_segments_on_strided_views():
+    """The strided entry point takes the schedule too: q, k, v, g as views of
+    one fused projection buffer, beta a strided column slice, out half of a
+    wider buffer, bit for bit the dense call's (both segmented), and against
+    the oracle."""
+    import torch
+    import gated_delta_rule_tok_amd as kda
+    from test_strided_gpu import SENTINEL, _strided_views
+    x = KI.make_inputs([1400, 600], 2, seed=88, init_state="fp32")
+    d = to_device(x)
+    kda.kda_debug_set_segment(256)
+    out_d, fin_d = run_gpu(x, d)
+    sd, out_s, obuf = _strided_views(d, "fused_rows")
+    _, fin_s, ws = alloc_outputs(x, d)
+    run_gpu(x, sd, out=out_s, fin=fin_s, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out_s.view(torch.int16), out_d.view(torch.int16)), "out differs"
+    assert torch.equal(fin_s, fin_d), "final state differs"
+    assert bool((obuf[..., :128].view(torch.int16) == SENTINEL).all()), "wrote outside out"
+    oref, fref = run_oracle(x)
+    assert_parity(x, out_s, fin_s, oref, fref, label="segments, strided views")
