@@ -110,7 +110,8 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 // wave w forms rows 16 w .. 16 w + 15 of each step's P S + R as one 16 x 16
 // accumulator tile, in fp32 MFMAs over the 128 keys.  P's rows go straight
 // from memory into the A operands (each lane reads 16-byte pieces of its
-// row; the key order inside the sum is the same permutation on both sides)
+// row, the four lanes of a row adjacent ones; the key order inside the sum
+// is the same permutation on both sides)
 // and are fetched two steps ahead with R, since one step's products are
 // shorter than a round trip to memory; S comes from a transposed LDS tile as
 // 16-byte rows.  The 8 column
@@ -139,8 +140,10 @@ __global__ __launch_bounds__(kCombThreads) void seg_combine_kernel(SegParams sp)
                         : static_cast<const float*>(sp.s0)[o];
   }
   const int f = sp.first[n], cnt = sp.count[n];
-  // Operands of a step in a ring of three register sets: P[16 w + l16][32 g4
-  // + 4 q .. + 3] (q = 0..7) as A operands, R in the accumulator layout.
+  // Operands of a step in a ring of three register sets: P[16 w + l16][16 q
+  // + 4 g4 .. + 3] (q = 0..7; the four lanes of a row read 64 contiguous
+  // bytes per load, one cache line per row and pair of loads) as A
+  // operands, R in the accumulator layout.
   // Step j (segment f + j, j <= cnt - 2) uses set j % 3, fetched at the top
   // of step j - 2.
   float4 pb[3][8];
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(kCombThreads) void seg_combine_kernel(SegParams sp)
     const float* Pm = R + DD;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      pb[b][q] = *reinterpret_cast<const float4*>(Pm + size_t(16 * w + l16) * kD + 32 * g4 + 4 * q);
+      pb[b][q] = *reinterpret_cast<const float4*>(Pm + size_t(16 * w + l16) * kD + 16 * q + 4 * g4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) rb[b][j] = R[size_t(row0 + j) * kD + col];
   };
@@ -174,10 +177,10 @@ __global__ __launch_bounds__(kCombThreads) void seg_combine_kernel(SegParams sp)
     for (int jj = 0; jj < 4; ++jj) St[l16][row0 + jj] = s[jj];  // S, transposed
     f32x4 acc = rb[b];
     __syncthreads();
-    // B operands S[32 g4 + 4 q + e][col]: the same key order as the A side
+    // B operands S[16 q + 4 g4 + e][col]: the same key order as the A side
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const float4 sv = *reinterpret_cast<const float4*>(&St[l16][32 * g4 + 4 * q]);
+      const float4 sv = *reinterpret_cast<const float4*>(&St[l16][16 * q + 4 * g4]);
       acc = mfma_f32(pb[b][q].x, sv.x, acc);
       acc = mfma_f32(pb[b][q].y, sv.y, acc);
       acc = mfma_f32(pb[b][q].z, sv.z, acc);
