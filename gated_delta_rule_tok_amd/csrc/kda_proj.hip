@@ -26,6 +26,8 @@
 // first 128 columns in slice order (so the result does not depend on the
 // schedule), rounds them to bf16 into LDS, writes its share of P, and forms
 // four 16 x 16 tiles of G from LDS against W_b.
+#include <algorithm>
+
 #include "kda_mfma.h"
 
 namespace kda {
@@ -52,11 +54,20 @@ __device__ __forceinline__ size_t part_index(const ProjParams& pp, int mt, int n
   return ((size_t(mt) * ntab + nt) * nsl + ks) * 256;
 }
 
-// First product: grid (K slices, row tiles of W_ab, token tiles), 4 waves.
+// First product: workgroup (K slice, row tile of W_ab, token tile), 4 waves.
+// The dispatcher hands workgroup B to XCD (B + o) mod 8, so index B = 8 r +
+// x carries slice ks = 8 (r / (row tiles x token tiles)) + x: every
+// workgroup of one K slice sits on one XCD and the slice of the hidden
+// states is fetched into that XCD's L2 once (indices past the last slice
+// exit).
 __global__ __launch_bounds__(64 * kAbWaves) void proj_ab_kernel(ProjParams pp) {
   __shared__ f32x4 red[kAbWaves][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int ks = blockIdx.x, nt = blockIdx.y, mt = blockIdx.z;
+  const int ntab = (pp.n_ab + 15) / 16, nmt = (pp.M + 15) / 16;
+  const int nsl = (pp.K + kSliceK - 1) / kSliceK;
+  const int r = blockIdx.x >> 3, nt = r % ntab, mt = (r / ntab) % nmt;
+  const int ks = 8 * (r / (ntab * nmt)) + (blockIdx.x & 7);
+  if (ks >= nsl) return;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int m = mt * 16 + l16;          // A operand row (token)
   const int n = nt * 16 + l16;          // B operand column (row of W_ab)
@@ -111,14 +122,19 @@ __device__ __forceinline__ void slice_sums(const float* const (&p)[NI], int nsl,
   }
 }
 
-// Second launch: grid (max(G column groups of 64, row tiles of W_ab), token
-// tiles), 4 waves.  Workgroup x writes P's column tile x (if there is one)
-// and G's column tiles 4x .. 4x + 3 (those that exist).
+// Second launch: workgroup (x, token tile mt), 4 waves, x up to the larger
+// of G's column groups of 64 and W_ab's row tiles.  Workgroup x writes P's
+// column tile x (if there is one) and G's column tiles 4x .. 4x + 3 (those
+// that exist).  Index B = 8 (mt X + x) + c works when c = mt mod 8 (the
+// others exit): a token tile's workgroups all sit on one XCD, which fetches
+// its partial tiles once.
 __global__ __launch_bounds__(256) void proj_out_kernel(ProjParams pp) {
   __shared__ __align__(16) uint16_t P[16][kLdsPitch];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int x = blockIdx.x, mt = blockIdx.y;
   const int ntab = (pp.n_ab + 15) / 16;
+  const int gx = max((pp.n_b / 16 + kWaves - 1) / kWaves, ntab);
+  const int r = blockIdx.x >> 3, x = r % gx, mt = r / gx;
+  if (int(blockIdx.x & 7) != (mt & 7)) return;
   const int gt = x * kWaves + w;  // this wave's G column tile
   const bool has_g = gt < pp.n_b / 16;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -194,13 +210,14 @@ hipError_t launch_proj(const ProjParams& p, hipStream_t stream) {
   ProjParams arg = p;
   void* args[] = {&arg};
   const int nmt = (p.M + 15) / 16, ntab = (p.n_ab + 15) / 16;
-  const dim3 g1((p.K + kSliceK - 1) / kSliceK, ntab, nmt);
+  const int nsl = (p.K + kSliceK - 1) / kSliceK;
+  const dim3 g1(8 * ((nsl + 7) / 8) * ntab * nmt);  // see proj_ab_kernel
   if (hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&proj_ab_kernel), g1,
                                      dim3(64 * kAbWaves), args, 0, stream);
       e != hipSuccess)
     return e;
-  const int gx = (p.n_b / 16 + kWaves - 1) / kWaves;
-  const dim3 g2(gx > ntab ? gx : ntab, nmt);
+  const int gx = std::max((p.n_b / 16 + kWaves - 1) / kWaves, ntab);
+  const dim3 g2(8 * gx * nmt);  // see proj_out_kernel
   return hipLaunchKernel(reinterpret_cast<const void*>(&proj_out_kernel), g2, dim3(64 * kWaves),
                          args, 0, stream);
 }
