@@ -650,3 +650,36 @@ def test_proj_brute_force_small_integers():
             assert p[m, n] == sum(h[m, k] * wab[n, k] for k in range(K))
         for n in range(nb):
             assert g[m, n] == sum(p[m, j] * wb[n, j] for j in range(128))
+
+
+def test_segment_maps_compose_to_the_one_pass_result(oracle_mod):
+    """The algebra of the segment-parallel schedule, in the oracle's fp64: the
+    recurrence is affine in the state, so a segment maps its entering state S
+    to P S + R, with P the segment run from the identity with zero values and
+    R the segment run from zero with its values.  Chaining S_{j+1} = P_j S_j +
+    R_j over the segments gives each segment's end state as a rerun from S_j
+    computes it, and the one-pass final state; the reruns' outputs are the
+    one-pass outputs.  Weak decay (lower_bound -0.3) keeps P far from zero, and
+    the segment bounds are not multiples of 16."""
+    x = KI.make_inputs([97], 2, seed=90, init_state="fp32", lower_bound=-0.3)
+    H = x.H
+    run = lambda sl, v, s0: oracle.kda_oracle_fwd(
+        x.q[sl], x.k[sl], v[sl], x.g[sl], x.beta_logits[sl], x.A_log, x.dt_bias,
+        x.lower_bound, x.scale, s0, np.array([0, sl.stop - sl.start], np.int32))
+    out1, fin1 = oracle.kda_oracle_fwd(x.q, x.k, x.v, x.g, x.beta_logits, x.A_log, x.dt_bias,
+                                       x.lower_bound, x.scale, x.initial_state, x.cu_seqlens)
+    zeros_v = np.zeros_like(x.v)
+    eye = np.broadcast_to(np.eye(128), (1, H, 128, 128)).copy()
+    S = x.initial_state.astype(np.float64)[0]
+    outs = np.zeros_like(out1)
+    for a, b in ((0, 30), (30, 64), (64, 97)):
+        sl = slice(a, b)
+        _, P = run(sl, zeros_v, eye)
+        _, R = run(sl, x.v, None)
+        o_seg, S_end = run(sl, x.v, S[None])
+        outs[sl] = o_seg
+        S = np.einsum("hij,hjk->hik", P[0], S) + R[0]
+        assert np.abs(P[0]).max() > 1e-3                      # the map carries the state
+        np.testing.assert_allclose(S, S_end[0], rtol=0, atol=1e-12 * max(1.0, np.abs(S).max()))
+    np.testing.assert_allclose(S, fin1[0], rtol=0, atol=1e-12 * max(1.0, np.abs(S).max()))
+    np.testing.assert_allclose(outs, out1, rtol=0, atol=1e-12 * max(1.0, np.abs(out1).max()))
