@@ -109,15 +109,20 @@ int plan_vsplit(int heads, int seqs, int cus) {
 // ---- the segment-parallel schedule (kda_segment.hip) ---------------------------
 // Long sequences in a call with few (sequence, head) items are cut into
 // segments that run in parallel.  Taken when there are at most
-// kSegItemsMax items, at least kSegMinAvg tokens per sequence on average and
-// the workspace holds the segment area.  The segment length aims at about
+// kSegItemsMax items, at least kSegMinAvg tokens per sequence on average
+// (twice that with more than kSegItemsMax / 2 items) and the workspace holds
+// the segment area.  The segment length aims at about
 // kSegTarget / heads segments in the call (so summaries and reruns fill the
 // machine), at least kSegMinLen tokens, a multiple of 64 (whole rounds of
-// four 16-token chunks).
+// four 16-token chunks).  Measured over shapes of 1-8 sequences of
+// 512-65536 tokens and 2-32 heads: at 1024 tokens per sequence 256-token
+// segments gain about 12% and 512-token ones lose (with 32 items every cut
+// loses there), at 512 tokens every cut loses; 64 items would fill the
+// machine with plain workgroups already.
 constexpr int kSegItemsMax = 32;
-constexpr int64_t kSegMinAvg = 2048;
+constexpr int64_t kSegMinAvg = 1024;
 constexpr int kSegTarget = 128;
-constexpr int kSegMinLen = 512;
+constexpr int kSegMinLen = 256;
 
 // Pseudo-sequences a call may use: a call that takes the schedule has at
 // most kSegItemsMax / heads sequences and kSegTarget / heads + its sequence
@@ -156,7 +161,8 @@ int plan_segment_len(int64_t T, int heads, int seqs, int forced) {
   if (forced > 1) {
     L = forced;
   } else {
-    if (int64_t(seqs) * heads > kSegItemsMax || T < kSegMinAvg * seqs) return 0;
+    const int64_t items = int64_t(seqs) * heads;
+    if (items > kSegItemsMax || T < kSegMinAvg * seqs * (2 * items > kSegItemsMax ? 2 : 1)) return 0;
     const int64_t target = kSegTarget / heads;
     L = (T + target - 1) / target;
     L = std::max<int64_t>(kSegMinLen, (L + 63) / 64 * 64);

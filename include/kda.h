@@ -84,7 +84,7 @@ typedef enum { KDA_STATE_FP32 = 0, KDA_STATE_BF16 = 1 } kda_state_dtype_t;
  *
  * The size has two parts.  A call needs the first (the status word and a
  * sequence order table, 4 bytes per sequence); with less it returns
- * KDA_ERR_WORKSPACE_TOO_SMALL.  The second (31.5 MB when max_tokens >= 2048,
+ * KDA_ERR_WORKSPACE_TOO_SMALL.  The second (31.5 MB when max_tokens >= 1024,
  * else none) holds the segment-parallel schedule: long
  * sequences in a call with at most 32 (sequence, head) pairs are cut into
  * segments that run at once (each segment's state map P S + R, then the
@@ -380,7 +380,8 @@ int kda_debug_set_vsplit(int s);
 /*
  * Test hook: the segment-parallel schedule -- 0 (default): automatic (at most
  * 32 (sequence, head) pairs and at least 2048 tokens per sequence on average,
- * segments of about 128 / heads per call, at least 512 tokens); 1: never;
+ * or at most 16 pairs and at least 1024 tokens; segments of about 128 / heads
+ * per call, at least 256 tokens); 1: never;
  * a multiple of 16 from 16 to 2^24: segments of that many tokens whenever
  * the pipelined 16-token kernel runs the call, heads <= 32 and the segment
  * area holds them ((sequences + num_tokens / len) * heads <= 160).

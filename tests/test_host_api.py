@@ -137,8 +137,8 @@ SEG_AREA = 2560 + 768 + 768 + 160 * 3 * 128 * 128 * 4
 def test_workspace_segment_area(heads):
     f = kda.kda_get_workspace_size
     base = 256 + 256
-    assert f(2047, heads, 8) == base                    # no call this small segments
-    assert f(2048, heads, 8) == base + SEG_AREA
+    assert f(1023, heads, 8) == base                    # no call this small segments
+    assert f(1024, heads, 8) == base + SEG_AREA
     assert f(1 << 20, heads, 1) == 256 + 256 + SEG_AREA  # independent of the token count
     assert SEG_AREA < 32 << 20
 
@@ -146,9 +146,15 @@ def test_workspace_segment_area(heads):
 @pytest.mark.parametrize("T,H,N,L", [
     (16384, 16, 1, 2048),    # 1 x 16384, 16 heads: 128 / 16 = 8 segments
     (16384, 4, 2, 512),      # 2 x 8192, 4 heads: 32 segments of 512
-    (8192, 4, 1, 512),       # at least 512 tokens
+    (8192, 4, 1, 256),       # 8192 / 32, at least 256 tokens
+    (1024, 4, 1, 256),       # at least 1024 tokens per sequence on average
+    (1023, 4, 1, 0),
+    (4096, 4, 8, 0),         # 512 tokens per sequence
+    (4096, 8, 4, 0),         # 32 pairs need 2048 tokens per sequence
+    (2048, 8, 2, 256),       # 16 pairs, 1024 tokens per sequence
+    (4096, 16, 2, 512),      # 32 pairs, 2048 tokens per sequence
     (16384, 16, 8, 0),       # 128 (sequence, head) pairs: one piece
-    (256, 2, 1, 0),          # fewer than 2048 tokens per sequence
+    (256, 2, 1, 0),          # fewer than 1024 tokens per sequence
     (65536, 32, 1, 16384),   # 128 / 32 = 4 segments; 1 + 4 pseudo-sequences x 32 <= 160
     (4096, 32, 1, 1024),     # the same cut at 4096 tokens
     (65536, 32, 2, 0),       # 64 (sequence, head) pairs: one piece

@@ -91,15 +91,16 @@ def test_forced_segments_match_oracle(L, state):
 
 def test_automatic_segments_on_long_low_parallelism():
     """1 x 8192 tokens, 4 heads: the automatic schedule cuts the sequence
-    (8192 / (128 / 4) = 256 -> segments of the minimum 512 tokens): its table
-    is in the workspace, and the result matches the oracle and the plain
-    schedule's.  (With the workloads' decay the plain and the segmented
+    (128 / 4 = 32 segments of 256 tokens): its table is in the workspace, and
+    the result matches the oracle and the plain schedule's.  (With the workloads' decay the plain and the segmented
     results are even bit-identical: a segment's transition underflows to zero
     within a few chunks, and what its entering state still contributes after
     the first chunk lies far below an fp32 unit of the state.)"""
     import torch
     import gated_delta_rule_tok_amd as kda
     x = KI.make_inputs([8192], 4, seed=82, init_state="fp32")
+    L = kda.kda_debug_segment_length(x.T, x.H, x.N)   # (automatic)
+    assert L == 256
     d = to_device(x)
     out_s, fin_s, ws = alloc_outputs(x, d)
     run_gpu(x, d, out=out_s, fin=fin_s, ws=ws)
@@ -109,10 +110,10 @@ def test_automatic_segments_on_long_low_parallelism():
     oref, fref = run_oracle(x)
     assert_parity(x, out_s, fin_s, oref, fref, label="automatic segments")
     assert_parity(x, out_p, fin_p, oref, fref, label="plain schedule")
-    M = 1 + 8192 // 512
+    M = 1 + 8192 // L
     off = 256 + _align(4 * x.N)
     table = ws[off:off + 16 * M].view(torch.int32).cpu().numpy().reshape(M, 4)
-    assert np.array_equal(table, _expected_table(x.cu_seqlens, x.T, 512, M)), "segment table"
+    assert np.array_equal(table, _expected_table(x.cu_seqlens, x.T, L, M)), "segment table"
     assert (out_s.view(torch.int16) != out_p.view(torch.int16)).float().mean().item() < 1e-3
 
 
