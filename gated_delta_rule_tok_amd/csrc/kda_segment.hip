@@ -111,10 +111,9 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 // accumulator tile, in fp32 MFMAs over the 128 keys.  P's rows go straight
 // from memory into the A operands (each lane reads 16-byte pieces of its
 // row, the four lanes of a row adjacent ones; the key order inside the sum
-// is the same permutation on both sides)
-// and are fetched two steps ahead with R, since one step's products are
-// shorter than a round trip to memory; S comes from a transposed LDS tile as
-// 16-byte rows.  The 8 column
+// is the same permutation on both sides) and are fetched two steps ahead
+// with R, since one step's products are shorter than a round trip to
+// memory; S comes from a transposed LDS tile as 16-byte rows.  The 8 column
 // blocks of one (n, h) go to one XCD (workgroup indices 8 apart), so each P
 // is fetched into that XCD's L2 once.
 __global__ __launch_bounds__(kCombThreads) void seg_combine_kernel(SegParams sp) {
