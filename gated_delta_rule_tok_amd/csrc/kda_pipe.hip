@@ -78,11 +78,20 @@ struct Cfg {
   static constexpr int kThreads = 64 * (kProdWaves + NSW);
 };
 
-// [128][16] tiles (row = key channel, column = token): rows are stored in the
-// order swz(r), which keeps both the producers' 16-byte row writes (8 lanes
-// write rows 4c + i, c = 0..3, two halves each) and the transposed operand
-// reads (4 consecutive rows x 32 bytes) on distinct banks.
+// [128][16] tiles (row = key channel, column = token; 32 bytes a row, four
+// 8-byte token groups).  Row r sits at position p = swz(r) and its token
+// group g at slot (g + p / 16) mod 4 of the row.  An 8-byte LDS access serves
+// 16 lanes at a time on 32 four-byte banks, so those 16 lanes must cover 16
+// distinct (p mod 4, slot) pairs.  The producers' stores (16 rows 4 c + i,
+// one token group) get them from the rotation -- without it their 16 rows
+// fell on 4 bank pairs, 4-way conflicts, most of the kernel's conflict
+// cycles -- and the transposed operand reads (4 consecutive rows x 4 token
+// groups) from the row order, which the rotation does not change.
 __device__ __forceinline__ int swz(int r) { return r ^ ((r >> 2) & 3); }
+__device__ __forceinline__ int tile(int r, int g) {  // element offset of row r, token group g
+  const int p = swz(r);
+  return p * kTok + 4 * ((g + (p >> 4)) & 3);
+}
 
 // Fragment tiles: the A-operand order of a 16x16x16 MFMA.  Element (row m,
 // column k) of 16x16 block b sits at (b * 64) + ((k / 4) * 16 + m) * 4 + k % 4,
@@ -359,7 +368,7 @@ __device__ __forceinline__ void produce_operands(Pack& pk, bf16* kg, Raw& raw,
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = 64 * hf + 4 * cg + i;
-    const int row = swz(c) * kTok + 4 * tq;  // this lane's 4 tokens of channel c
+    const int row = tile(c, tq);  // this lane's 4 tokens of channel c
     const float g16 = kKpScale * gam[i];
     float vx[4], vq[4], vg[4], vk[4];
 #pragma unroll
@@ -390,11 +399,10 @@ __device__ __forceinline__ void produce_inverse(Pack& pk, const bf16* kg, int la
   // k-slots 8 g4 .. 8 g4 + 7 of each 32-channel block, on both sides
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 accA = zero, accAt = zero;
-  const int col = 4 * (l16 & 3);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const int r1 = 32 * kb + 8 * g4 + (l16 >> 2), r2 = r1 + 4;
-    const int o1 = swz(r1) * kTok + col, o2 = swz(r2) * kTok + col;
+    const int o1 = tile(r1, l16 & 3), o2 = tile(r2, l16 & 3);
     const bf16x8 KE = cat(tr4(&pk.x[o1]), tr4(&pk.x[o2]));
     const bf16x8 KG = cat(tr4(&kg[o1]), tr4(&kg[o2]));
     accA = mfma32(KE, KG, accA);     // [t = 4g4+j][i = l16]
@@ -435,11 +443,10 @@ __device__ __forceinline__ void produce_inverse(Pack& pk, const bf16* kg, int la
 __device__ __forceinline__ void produce_m(Pack& pk, const bf16* kg, int lane) {
   const int l16 = lane & 15, g4 = lane >> 4;
   f32x4 accMt = {0.f, 0.f, 0.f, 0.f};
-  const int col = 4 * (l16 & 3);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const int r1 = 32 * kb + 8 * g4 + (l16 >> 2), r2 = r1 + 4;
-    const int o1 = swz(r1) * kTok + col, o2 = swz(r2) * kTok + col;
+    const int o1 = tile(r1, l16 & 3), o2 = tile(r2, l16 & 3);
     const bf16x8 KG = cat(tr4(&kg[o1]), tr4(&kg[o2]));
     const bf16x8 QE = cat(tr4(&pk.qt[o1]), tr4(&pk.qt[o2]));
     accMt = mfma32(KG, QE, accMt);   // [i = 4g4+j][t = l16]
@@ -802,11 +809,10 @@ __global__ __launch_bounds__(Cfg<VS>::kThreads, 1) void pipe_kernel(Params p) {
       // X and Q_T as A operands; k-slots {32kb + 4g4 + j, 32kb + 16 + 4g4 + j}
       // match the B operand built from two accumulator tiles of S
       bf16x8 ax[4], aq[4];
-      const int col = 4 * (l16 & 3);
 #pragma unroll
       for (int kb2 = 0; kb2 < 4; ++kb2) {
         const int r1 = 32 * kb2 + 4 * g4 + (l16 >> 2), r2 = r1 + 16;
-        const int o1 = swz(r1) * kTok + col, o2 = swz(r2) * kTok + col;
+        const int o1 = tile(r1, l16 & 3), o2 = tile(r2, l16 & 3);
         ax[kb2] = cat(tr4(&P.x[o1]), tr4(&P.x[o2]));
         if constexpr (!SUMM) aq[kb2] = cat(tr4(&P.qt[o1]), tr4(&P.qt[o2]));
       }
