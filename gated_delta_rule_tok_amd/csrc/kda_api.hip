@@ -128,6 +128,23 @@ constexpr int kSegMinLen = 256;
 // most kSegItemsMax / heads sequences and kSegTarget / heads + its sequence
 // count segments, so pseudo-sequences x heads <= kSegSlots.
 constexpr int kSegSlots = kSegItemsMax + kSegTarget;
+
+// ---- the two-workgroup forward (kda_duo.hip) ------------------------------------
+// A producer and a consumer workgroup per (sequence, head) item, all of them
+// on the device at once: taken for more than kDuoItemsMin and at most
+// kDuoItemsMax items with 2 items <= CUs (where the single-workgroup kernel
+// splits the values and repeats each item's state-independent work) and at
+// most kDuoWorkMax (token, head) pairs in the call, when the workspace holds
+// the segment area (the package rings and flag words live there).  Measured
+// over 40-128 items of 128-2048 tokens: 3-13% faster up to 2^17 (token,
+// head) pairs (e.g. 128 items x 512 tokens 42 against 46 us, 64 x 2048
+// 121 against 128 us), slower above (96 x 2048 135 against 131 us,
+// 128 x 2048 164 against 138 us: there the handoff of every package through
+// L2 costs more than the repeated producer work).
+constexpr int kDuoItemsMin = 32;
+constexpr int kDuoItemsMax = 128;
+constexpr int64_t kDuoWorkMax = int64_t(1) << 17;
+std::atomic<uint32_t> g_duo_nonce{0x2545f491u};
 int seg_cap(int heads) { return heads <= kSegItemsMax ? kSegSlots / heads : 0; }
 
 // The segment area, one size for every head count (so the workspace size
@@ -135,7 +152,7 @@ int seg_cap(int heads) { return heads <= kSegItemsMax ? kSegSlots / heads : 0; }
 // pseudo-sequences, and kSegSlots (pseudo-sequence, head) slots of summaries
 // (local state, transition) and entering states, fp32 128 x 128 each.
 struct SegLayout {
-  size_t table, first, count, summ, starts, bytes;
+  size_t table, first, count, summ, starts, duo_flags, bytes;
 };
 constexpr size_t kDD = size_t(KDA_HEAD_DIM) * KDA_HEAD_DIM * sizeof(float);
 SegLayout seg_layout() {
@@ -145,9 +162,14 @@ SegLayout seg_layout() {
   l.count = l.first + align_up(4 * size_t(kSegSlots));
   l.summ = l.count + align_up(4 * size_t(kSegSlots));
   l.starts = l.summ + size_t(kSegSlots) * 2 * kDD;
-  l.bytes = l.starts + size_t(kSegSlots) * kDD;
+  l.duo_flags = l.starts + size_t(kSegSlots) * kDD;
+  l.bytes = l.duo_flags + align_up(kda::kDuoFlagWords * sizeof(uint64_t) * size_t(kDuoItemsMax));
   return l;
 }
+// The two-workgroup forward's package rings share the space of the
+// summaries and entering states (a call takes one schedule or the other).
+static_assert(size_t(kDuoItemsMax) * kda::kDuoRing * kda::kDuoPkgBytes <= size_t(kSegSlots) * 3 * kDD,
+              "the package rings fit in the summaries' and entering states' space");
 
 // Status word and the sequence order table.
 size_t base_workspace_bytes(int32_t seqs) { return kAlign + align_up(sizeof(int32_t) * size_t(seqs)); }
@@ -199,8 +221,9 @@ const char* kda_last_hip_error(void) { return t_last_hip_error; }
 
 int kda_debug_set_kernel(int k) {
   // 0 automatic, 1 64-token chunk, 2 token-serial, 3 token-serial decode
-  // staging (4 tokens), 4 pipelined 16-token, 5 pipelined 32-token
-  if (k < 0 || k > 5) return -1;
+  // staging (4 tokens), 4 pipelined 16-token in one workgroup per item, 5
+  // pipelined 32-token, 6 pipelined 16-token in two workgroups per item
+  if (k < 0 || k > 6) return -1;
   return g_kernel_override.exchange(k);
 }
 
@@ -364,14 +387,18 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   // columns: below that bound the 32-token kernel, an unsplit launch (test
   // hook) the 64-token kernel.  Both pipelined kernels split the value
   // dimension at least in two when the rule says unsplit (a 128-column slice
-  // holds more state than their waves' registers: measured slower)
+  // holds more state than their waves' registers: measured slower; the
+  // two-workgroup form below is the unsplit one).  Kernel 6 (the two-workgroup
+  // form on request) falls back to the 16-token kernel where it cannot run.
+  const bool want_duo = kernel == 6;
+  if (kernel == 6) kernel = 4;
   if (kernel == 4 && lower_bound < kda::kPipeLowerBoundMin) kernel = 5;
   if ((kernel == 4 || kernel == 5) && p.vsplit == 1 && forced == 0) p.vsplit = 2;
   if (kernel == 4 && p.vsplit == 1) kernel = 1;
   if (checkpoints && kernel != 4 && kernel != 5) return KDA_ERR_UNSUPPORTED;
 
   // segment-parallel schedule: summaries, combine, rerun (kda_segment.hip)
-  if (kernel == 4 && !checkpoints && !sp_idx && !fixed_scratch &&
+  if (kernel == 4 && !want_duo && !checkpoints && !sp_idx && !fixed_scratch &&
       reinterpret_cast<uintptr_t>(workspace) % 16 == 0) {
     const int L = plan_segment_len(num_tokens, heads, num_seqs,
                                    g_segment_override.load(std::memory_order_relaxed));
@@ -417,6 +444,28 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
       pc.s0 = sp.starts;
       if (hipError_t e = kda::launch_pipe(pc, st); e != hipSuccess)
         return hip_failure(e, "segment rerun launch");
+      return KDA_OK;
+    }
+  }
+
+  // two-workgroup forward: automatic in its range of item counts, or on
+  // request (kernel 6, any count that fits; else the plain kernel)
+  if (kernel == 4 && !checkpoints && !sp_idx && !fixed_scratch &&
+      reinterpret_cast<uintptr_t>(workspace) % 16 == 0 && forced == 0) {
+    const int64_t items = int64_t(num_seqs) * heads;
+    const SegLayout lay = seg_layout();
+    const size_t off = base_workspace_bytes(num_seqs);
+    const bool fits = items <= kDuoItemsMax && 2 * items <= cus && workspace_bytes >= off + lay.bytes;
+    if (fits && (want_duo || (items > kDuoItemsMin && num_tokens * heads <= kDuoWorkMax))) {
+      char* w = static_cast<char*>(workspace) + off;
+      p.duo_ring = w + lay.summ;
+      p.duo_flags = reinterpret_cast<uint64_t*>(w + lay.duo_flags);
+      uint32_t nonce = 0;
+      while (nonce == 0) nonce = g_duo_nonce.fetch_add(0x9e3779b9u, std::memory_order_relaxed);
+      p.duo_nonce = nonce;
+      p.order = nullptr;
+      if (hipError_t e = kda::launch_duo(p, st); e != hipSuccess)
+        return hip_failure(e, "two-workgroup kernel launch");
       return KDA_OK;
     }
   }

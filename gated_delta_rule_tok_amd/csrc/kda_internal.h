@@ -69,7 +69,19 @@ struct Params {
   //     last segments only.
   const int32_t* seg;
   int seg_mode;
+  // two-workgroup forward (kda_duo.hip): per item, kDuoRing chunk packages of
+  // kDuoPkgBytes (duo_ring) and kDuoFlagWords flag words (duo_flags);
+  // duo_nonce marks this call's flag words
+  void* duo_ring;
+  uint64_t* duo_flags;
+  uint32_t duo_nonce;
 };
+
+// The two-workgroup forward: packages per item in flight between its two
+// workgroups, and their size in the workspace (a package rounded up to 1 KB).
+constexpr int kDuoRing = 8;
+constexpr int kDuoPkgBytes = 14336;
+constexpr int kDuoFlagWords = 8;  // uint64 flag words per (sequence, head)
 
 // Pseudo-sequences of the segment-parallel schedule (kda_segment.hip).  Each
 // sequence n is cut into count[n] = max(1, ceil(len / L)) segments of L tokens
@@ -151,6 +163,13 @@ constexpr float kPipeLowerBoundMin = -5.0f;
 constexpr int kDecodeTokensPerSeq = 8;
 constexpr int kInlineRankMax = 16;
 hipError_t launch_pipe(const Params& p, hipStream_t stream);
+
+// The same 16-token forward with the producers and the state waves in two
+// workgroups of one XCD per (sequence, head): 2 * 8 ceil(N H / 8) workgroups,
+// which must all fit on the device at once (2 N H <= CUs); all 128 value
+// columns in one workgroup, the packages through p.duo_ring, p.duo_flags
+// (N H entries each) and the call's p.duo_nonce.  Lower bound as above.
+hipError_t launch_duo(const Params& p, hipStream_t stream);
 
 // Pipelined 32-token chunk forward (two 16-token halves with their own decay
 // reference points): four producer waves build the packages of alternating

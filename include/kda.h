@@ -405,7 +405,12 @@ int32_t kda_debug_segment_length(int64_t num_tokens, int32_t heads, int32_t num_
  * (num_tokens <= 8 * num_seqs: decode-sized) takes the token-serial kernel
  * with 4-token staging, whatever its longest sequence; any other call the
  * pipelined 16-token chunk kernel for lower_bound >= -5, else the pipelined
- * 32-token kernel, both with the value dimension split at least in two.  The
+ * 32-token kernel, both with the value dimension split at least in two, except
+ * that the 16-token kernel runs in two workgroups per (sequence, head) (a
+ * producer and a consumer of all 128 value columns, bit for bit the same
+ * results) for 33 to 128 (sequence, head) pairs when twice the pair count fits
+ * on the device's compute units, the call has at most 2^17 (token, head)
+ * pairs and the workspace holds its second part.  The
  * choice is by the batch's average, so one sequence's result may come from
  * either kernel depending on what it is batched with: both follow the
  * recurrence within the tolerances of the oracle, but they are not bit for
@@ -417,8 +422,12 @@ int32_t kda_debug_segment_length(int64_t num_tokens, int32_t heads, int32_t num_
  * size (lower_bound < -5 goes to the 32-token kernel, a forced unsplit launch
  * to the 64-token kernel); 5: the pipelined 32-token kernel (chunks of two
  * 16-token halves, each with its own decay reference) whatever the call's
- * size.  Process-wide.  Returns the previous setting, or -1 (unchanged) for
- * an invalid value.
+ * size; 6: the 16-token kernel in two workgroups per pair for any pair count
+ * that fits (at most 128 pairs and twice the pair count within the compute
+ * units; the workspace's second part present; no checkpoints), else as 4.  A
+ * kda_debug_set_vsplit override keeps the 16-token kernel in one workgroup per
+ * value slice.  Process-wide.  Returns the previous setting, or -1
+ * (unchanged) for an invalid value.
  */
 int kda_debug_set_kernel(int k);
 

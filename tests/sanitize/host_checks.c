@@ -120,7 +120,7 @@ int main(void) {
   // status strings and the test hooks
   for (int c = -1; c <= 6; ++c) /* also values outside the enumerators */
     if (!kda_status_string((kda_status_t)c) || !strlen(kda_status_string((kda_status_t)c))) ++failures;
-  expect(kda_debug_set_kernel(6), -1, "invalid kernel selector");
+  expect(kda_debug_set_kernel(7), -1, "invalid kernel selector");
   expect(kda_debug_set_vsplit(3), -1, "invalid split");
   expect(strlen(kda_last_hip_error()) == 0, 1, "no HIP error recorded");
 

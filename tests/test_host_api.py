@@ -130,7 +130,7 @@ def test_workspace_too_small():
 # The segment area: 160 table entries (16 bytes), first/count ints, and 160
 # (pseudo-sequence, head) slots of a summary (local state and transition) and
 # an entering state, fp32 128 x 128 each; the same for every head count.
-SEG_AREA = 2560 + 768 + 768 + 160 * 3 * 128 * 128 * 4
+SEG_AREA = 2560 + 768 + 768 + 160 * 3 * 128 * 128 * 4 + 128 * 8 * 8  # + the two-workgroup flag words
 
 
 @pytest.mark.parametrize("heads", [1, 2, 3, 4, 16, 32, 33, 64])
@@ -290,9 +290,9 @@ def test_python_binding_never_copies_parameters():
 
 def test_debug_kernel_hook():
     lib = kda.load_library()
-    for k in (1, 2, 3, 4, 5, 0):
+    for k in (1, 2, 3, 4, 5, 6, 0):
         assert lib.kda_debug_set_kernel(k) >= 0
-    assert lib.kda_debug_set_kernel(6) == -1
+    assert lib.kda_debug_set_kernel(7) == -1
     assert lib.kda_debug_set_kernel(-1) == -1
     assert lib.kda_debug_set_kernel(0) == 0
 
