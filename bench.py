@@ -58,18 +58,22 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def dominant_kernel(decode: bool, lower_bound: float, seg_len: int = 0, vs: int = 64) -> str:
+def dominant_kernel(decode: bool, lower_bound: float, seg_len: int = 0, vs: int = 64,
+                    duo: bool = False) -> str:
     """The kernels a call's time goes to (the library's automatic choice):
     the token-serial decode kernel for decode-sized calls, else the 16-token
     pipelined kernel for lower_bound >= -5 and the 32-token one below.  A call
     that takes the segment-parallel schedule (seg_len > 0) runs four kernels,
-    named "+"-joined as rocprofv3 prints them (vs: the rerun's value slice)."""
+    named "+"-joined as rocprofv3 prints them (vs: the rerun's value slice);
+    one that takes the two-workgroup form (duo) runs duo_kernel."""
     if decode:
         return "decode_kernel"
     if lower_bound < -5.0:
         return "fwd32_kernel"
     if seg_len:
         return f"seg_plan_kernel+pipe_kernel<64, true>+seg_combine_kernel+pipe_kernel<{vs}, false>"
+    if duo:
+        return "duo_kernel"
     return "pipe_kernel"
 
 
@@ -91,7 +95,25 @@ def call_kernels(args, T: int, H: int, N: int, lower_bound: float) -> str:
     if L:
         s = args.vsplit or max(2, plan_vsplit(H, N + T // L))
         vs = 128 // s
-    return dominant_kernel(decode, lower_bound, L, vs)
+    duo = (not decode and not args.checkpoint_interval and not L
+           and kda.kda_debug_two_workgroups(T, H, N, device_cus()))
+    return dominant_kernel(decode, lower_bound, L, vs, duo)
+
+
+def device_cus() -> int:
+    """Compute units of the GPU (256 on MI355X; 256 without a GPU)."""
+    import torch
+    if torch.cuda.is_available():
+        return torch.cuda.get_device_properties(0).multi_processor_count
+    return 256
+
+
+def uniform_dims(spec: str):
+    """--uniform N,L,H: N sequences of L tokens, H heads."""
+    n, length, h = (int(v) for v in spec.split(","))
+    if n <= 0 or length <= 0 or h <= 0:
+        raise ValueError(f"--uniform {spec}: sizes must be positive")
+    return n, length, h
 
 
 def traffic_file(workload: str, kernel: str) -> str:
@@ -151,6 +173,12 @@ def workload_name(args, dims=None):
     if args.decode_batch:
         wl, lb = f"decode_{args.decode_batch}x1_h16", KI.LOWER_BOUND
         sel = f"--decode-batch {args.decode_batch}"
+    elif getattr(args, "uniform", None):
+        n, length, h = uniform_dims(args.uniform)
+        wl, lb = f"uniform_{n}x{length}_h{h}", KI.LOWER_BOUND
+        sel = f"--uniform {n},{length},{h}"
+        if dims is None:
+            dims = (n * length, h, n)
     else:
         wl, lb = KI.CONFIGS[args.config]["name"], KI.LOWER_BOUND
         sel = f"--config {args.config}"
@@ -345,6 +373,9 @@ def main():
     ap.add_argument("--decode-batch", type=int, default=0,
                     help="instead of --config: this many one-token sequences, 16 heads, fp32 "
                          "state (a decode step; the token-serial decode kernel runs)")
+    ap.add_argument("--uniform", metavar="N,L,H", default=None,
+                    help="instead of --config: N sequences of L tokens, H heads, fp32 initial "
+                         "and final state, the configurations' input distributions")
     ap.add_argument("--settle-ms", type=float, default=200.0,
                     help="run the call this long before the warmup steps (clock ramp; 0: none)")
     ap.add_argument("--traffic-from", metavar="PMC_DIR",
@@ -405,6 +436,9 @@ def main():
     apply_hooks(args)
     if args.decode_batch:
         x = KI.make_inputs([1] * args.decode_batch, 16, seed=7, init_state="fp32")
+    elif args.uniform:
+        n, length, h = uniform_dims(args.uniform)
+        x = KI.make_inputs([length] * n, h, seed=11, init_state="fp32")
     else:
         x = KI.config_inputs(args.config)
     if args.lower_bound is not None:

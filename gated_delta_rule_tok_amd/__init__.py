@@ -21,7 +21,7 @@ import os
 
 __all__ = ["kda_get_workspace_size", "kda_chunk_prefill_fwd", "kda_status_string",
            "kda_workspace_status",
-           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel", "kda_debug_set_segment", "kda_debug_segment_length", "kda_spec_decode_step", "kda_chunk_prefill_fwd_noalloc", "kda_gate_proj",
+           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel", "kda_debug_set_segment", "kda_debug_segment_length", "kda_debug_two_workgroups", "kda_spec_decode_step", "kda_chunk_prefill_fwd_noalloc", "kda_gate_proj",
            "kda_gate_proj_workspace_size", "KdaError", "library_path", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -110,6 +110,8 @@ def load_library():
         lib.kda_debug_set_segment.restype = ctypes.c_int
         lib.kda_debug_segment_length.argtypes = [I64, I32, I32]
         lib.kda_debug_segment_length.restype = I32
+        lib.kda_debug_two_workgroups.argtypes = [I64, I32, I32, I32]
+        lib.kda_debug_two_workgroups.restype = I32
         _lib = lib
     return _lib
 
@@ -165,6 +167,14 @@ def kda_debug_set_segment(length: int) -> int:
 def kda_debug_segment_length(num_tokens: int, heads: int, num_seqs: int) -> int:
     """The segment length a call of these sizes would use (0: one piece)."""
     return int(load_library().kda_debug_segment_length(int(num_tokens), int(heads), int(num_seqs)))
+
+
+def kda_debug_two_workgroups(num_tokens: int, heads: int, num_seqs: int, cus: int = 256) -> bool:
+    """Whether a call of these sizes (with the workspace's second part) runs
+    the 16-token kernel in two workgroups per (sequence, head) on a device of
+    cus compute units."""
+    return bool(load_library().kda_debug_two_workgroups(int(num_tokens), int(heads), int(num_seqs),
+                                                        int(cus)))
 
 
 def _check(t, name, dtype, shape=None, strided=False):

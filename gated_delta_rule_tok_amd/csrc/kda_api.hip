@@ -145,6 +145,14 @@ constexpr int kDuoItemsMin = 32;
 constexpr int kDuoItemsMax = 128;
 constexpr int64_t kDuoWorkMax = int64_t(1) << 17;
 std::atomic<uint32_t> g_duo_nonce{0x2545f491u};
+
+// Whether a call of the 16-token family with the workspace's second part
+// takes the two-workgroup form (forced: on request, kernel 6).
+bool duo_rule(int64_t T, int heads, int seqs, int cus, bool forced) {
+  const int64_t items = int64_t(seqs) * heads;
+  if (items <= 0 || items > kDuoItemsMax || 2 * items > cus) return false;
+  return forced || (items > kDuoItemsMin && T * heads <= kDuoWorkMax);
+}
 int seg_cap(int heads) { return heads <= kSegItemsMax ? kSegSlots / heads : 0; }
 
 // The segment area, one size for every head count (so the workspace size
@@ -236,6 +244,17 @@ int kda_debug_set_segment(int len) {
 int32_t kda_debug_segment_length(int64_t num_tokens, int32_t heads, int32_t num_seqs) {
   if (num_tokens < 0 || heads <= 0 || num_seqs <= 0) return 0;
   return plan_segment_len(num_tokens, heads, num_seqs, g_segment_override.load(std::memory_order_relaxed));
+}
+
+int32_t kda_debug_two_workgroups(int64_t num_tokens, int32_t heads, int32_t num_seqs, int32_t cus) {
+  if (num_tokens < 0 || heads <= 0 || num_seqs <= 0 || cus <= 0) return 0;
+  const int k = g_kernel_override.load(std::memory_order_relaxed);
+  if (g_vsplit_override.load(std::memory_order_relaxed) != 0 || !(k == 0 || k == 4 || k == 6)) return 0;
+  if (k != 6 && num_tokens <= kda::kDecodeTokensPerSeq * int64_t(num_seqs)) return 0;  // decode-sized
+  if (k != 6 && plan_segment_len(num_tokens, heads, num_seqs,
+                                 g_segment_override.load(std::memory_order_relaxed)) > 0)
+    return 0;  // the segment-parallel schedule comes first
+  return duo_rule(num_tokens, heads, num_seqs, cus, k == 6) ? 1 : 0;
 }
 
 int kda_debug_set_vsplit(int s) {
@@ -452,11 +471,9 @@ kda_status_t forward(const void* q, const void* k, const void* v, const void* g,
   // request (kernel 6, any count that fits; else the plain kernel)
   if (kernel == 4 && !checkpoints && !sp_idx && !fixed_scratch &&
       reinterpret_cast<uintptr_t>(workspace) % 16 == 0 && forced == 0) {
-    const int64_t items = int64_t(num_seqs) * heads;
     const SegLayout lay = seg_layout();
     const size_t off = base_workspace_bytes(num_seqs);
-    const bool fits = items <= kDuoItemsMax && 2 * items <= cus && workspace_bytes >= off + lay.bytes;
-    if (fits && (want_duo || (items > kDuoItemsMin && num_tokens * heads <= kDuoWorkMax))) {
+    if (workspace_bytes >= off + lay.bytes && duo_rule(num_tokens, heads, num_seqs, cus, want_duo)) {
       char* w = static_cast<char*>(workspace) + off;
       p.duo_ring = w + lay.summ;
       p.duo_flags = reinterpret_cast<uint64_t*>(w + lay.duo_flags);

@@ -431,6 +431,15 @@ int32_t kda_debug_segment_length(int64_t num_tokens, int32_t heads, int32_t num_
  */
 int kda_debug_set_kernel(int k);
 
+/*
+ * Test hook (host only, no device access): 1 if a call with these sizes,
+ * lower_bound >= -5, no checkpoints and a workspace with its second part
+ * takes the two-workgroup form of the 16-token kernel on a device with cus
+ * compute units under the current kda_debug_* settings, else 0 (also for
+ * invalid sizes).
+ */
+int32_t kda_debug_two_workgroups(int64_t num_tokens, int32_t heads, int32_t num_seqs, int32_t cus);
+
 #ifdef __cplusplus
 }
 #endif

@@ -69,7 +69,7 @@ def test_bench_labels_the_segmented_workloads():
     import argparse
     import bench
     a = argparse.Namespace(proj=0, decode_batch=0, config=2, lower_bound=None, segments="auto",
-                           vsplit=0, checkpoint_interval=0)
+                           vsplit=0, checkpoint_interval=0, uniform=None)
     assert bench.workload_name(a)[1].startswith("seg_plan_kernel+")
     a.config = 3
     assert bench.workload_name(a)[1].startswith("seg_plan_kernel+")
@@ -79,3 +79,19 @@ def test_bench_labels_the_segmented_workloads():
     assert bench.workload_name(a)[1] == "pipe_kernel"
     a.segments = "auto"
     bench.apply_hooks(a)
+
+
+def test_bench_labels_the_two_workgroup_workloads():
+    """A uniform workload in the two-workgroup form's range is labelled with
+    its kernel; the 8 x 2048, 16-head configuration is not in that range."""
+    import argparse
+    import bench
+    a = argparse.Namespace(proj=0, decode_batch=0, config=1, lower_bound=None, segments="auto",
+                           vsplit=0, checkpoint_interval=0, uniform="32,512,4")
+    wl, kern, sel = bench.workload_name(a)
+    assert (wl, kern, sel) == ("uniform_32x512_h4", "duo_kernel", "--uniform 32,512,4")
+    a.uniform = None
+    assert bench.workload_name(a)[1] == "pipe_kernel"
+    a.uniform, a.vsplit = "32,512,4", 2
+    assert bench.workload_name(a)[1] == "pipe_kernel"
+    bench.apply_hooks(argparse.Namespace(segments="auto", vsplit=0))

@@ -35,6 +35,7 @@ def test_library_exports_every_declared_symbol():
                           "kda_status_string",
                           "kda_last_hip_error", "kda_debug_set_vsplit", "kda_debug_set_kernel",
                           "kda_debug_set_segment", "kda_debug_segment_length",
+                          "kda_debug_two_workgroups",
                           "kda_spec_decode_step", "kda_chunk_prefill_fwd_noalloc",
                           "kda_gate_proj", "kda_gate_proj_workspace_size"}
     for n in names:
@@ -383,3 +384,33 @@ def test_proj_workspace_checks():
     assert kda.kda_gate_proj_workspace_size(-1, 7168, 144) == 0
     assert kda.kda_gate_proj_workspace_size(17, 7168, 144) == 2 * 7 * 9 * 256 * 4  # two token tiles
     assert kda.kda_gate_proj_workspace_size(5, 1000, 136) == 1 * 9 * 256 * 4       # ragged K and n_ab
+
+
+def test_two_workgroup_rule():
+    """The two-workgroup form: 33-128 pairs that fit twice on the device and
+    at most 2^17 (token, head) pairs, after the decode and segment rules;
+    kernel 6 forces it wherever it fits; a value-split override keeps the
+    single-workgroup kernel."""
+    f = kda.kda_debug_two_workgroups
+    assert not f(16384, 16, 8)               # 128 pairs x 2048 tokens: 2^18 token-heads
+    assert f(8192, 16, 4)                    # 64 pairs x 2048
+    assert f(16384, 4, 32)                   # 128 pairs x 512
+    assert not f(8192, 16, 2)                # 32 pairs (the segment schedule takes it)
+    assert not f(2048, 4, 8)                 # 32 pairs
+    assert f(2816, 3, 11)                    # 33 pairs
+    assert not f(20000, 3, 50)               # 150 pairs: more than 128
+    assert not f(16384, 4, 32, cus=200)      # 2 x 128 pairs do not fit on 200 CUs
+    assert not f(256, 16, 40)                # decode-sized (6.4 tokens per sequence)
+    assert not f(0, 0, 1) and not f(-1, 1, 1)
+    lib = kda.load_library()
+    try:
+        lib.kda_debug_set_kernel(6)
+        assert f(300, 2, 1) and f(16384, 16, 8) and not f(16384, 16, 9)
+        lib.kda_debug_set_kernel(5)
+        assert not f(8192, 16, 4)
+        lib.kda_debug_set_kernel(0)
+        lib.kda_debug_set_vsplit(2)
+        assert not f(8192, 16, 4)
+    finally:
+        lib.kda_debug_set_kernel(0)
+        lib.kda_debug_set_vsplit(0)
