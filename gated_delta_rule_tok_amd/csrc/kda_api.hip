@@ -133,15 +133,18 @@ constexpr int kSegSlots = kSegItemsMax + kSegTarget;
 // A producer and a consumer workgroup per (sequence, head) item, all of them
 // on the device at once: taken for more than kDuoItemsMin and at most
 // kDuoItemsMax items with 2 items <= CUs (where the single-workgroup kernel
-// splits the values and repeats each item's state-independent work) and at
-// most kDuoWorkMax (token, head) pairs in the call, when the workspace holds
-// the segment area (the package rings and flag words live there).  Measured
-// over 40-128 items of 128-2048 tokens: 3-13% faster up to 2^17 (token,
-// head) pairs (e.g. 128 items x 512 tokens 42 against 46 us, 64 x 2048
-// 121 against 128 us), slower above (96 x 2048 135 against 131 us,
-// 128 x 2048 164 against 138 us: there the handoff of every package through
-// L2 costs more than the repeated producer work).
+// splits the values and repeats each item's state-independent work), above
+// kDuoItemsAny items only up to kDuoWorkMax (token, head) pairs in the call,
+// when the workspace holds the segment area (the package rings and flag
+// words live there).  Measured over 32-128 items of 128-4096 tokens: faster
+// or equal up to 96 items at every length (64 items x 4096 tokens 240
+// against 248 us, 96 x 2048 124 against 130) and above that for short
+// sequences (128 x 1024 69 against 72, 128 x 512 41 against 46, 128 x 256
+// 27 against 31), slower for 112-128 items of 2048 tokens (145 against 135,
+// 151 against 140: the packages' L2 traffic there costs more than the
+// repeated producer work).
 constexpr int kDuoItemsMin = 32;
+constexpr int kDuoItemsAny = 96;
 constexpr int kDuoItemsMax = 128;
 constexpr int64_t kDuoWorkMax = int64_t(1) << 17;
 std::atomic<uint32_t> g_duo_nonce{0x2545f491u};
@@ -151,7 +154,7 @@ std::atomic<uint32_t> g_duo_nonce{0x2545f491u};
 bool duo_rule(int64_t T, int heads, int seqs, int cus, bool forced) {
   const int64_t items = int64_t(seqs) * heads;
   if (items <= 0 || items > kDuoItemsMax || 2 * items > cus) return false;
-  return forced || (items > kDuoItemsMin && T * heads <= kDuoWorkMax);
+  return forced || (items > kDuoItemsMin && (items <= kDuoItemsAny || T * heads <= kDuoWorkMax));
 }
 int seg_cap(int heads) { return heads <= kSegItemsMax ? kSegSlots / heads : 0; }
 

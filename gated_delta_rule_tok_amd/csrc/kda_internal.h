@@ -79,7 +79,7 @@ struct Params {
 
 // The two-workgroup forward: packages per item in flight between its two
 // workgroups, and their size in the workspace (a package rounded up to 1 KB).
-constexpr int kDuoRing = 8;
+constexpr int kDuoRing = 4;
 constexpr int kDuoPkgBytes = 14336;
 constexpr int kDuoFlagWords = 8;  // uint64 flag words per (sequence, head)
 

@@ -408,9 +408,9 @@ int32_t kda_debug_segment_length(int64_t num_tokens, int32_t heads, int32_t num_
  * 32-token kernel, both with the value dimension split at least in two, except
  * that the 16-token kernel runs in two workgroups per (sequence, head) (a
  * producer and a consumer of all 128 value columns, bit for bit the same
- * results) for 33 to 128 (sequence, head) pairs when twice the pair count fits
- * on the device's compute units, the call has at most 2^17 (token, head)
- * pairs and the workspace holds its second part.  The
+ * results) for 33 to 96 (sequence, head) pairs, and for 97 to 128 pairs in
+ * calls of at most 2^17 (token, head) pairs, when twice the pair count fits
+ * on the device's compute units and the workspace holds its second part.  The
  * choice is by the batch's average, so one sequence's result may come from
  * either kernel depending on what it is batched with: both follow the
  * recurrence within the tolerances of the oracle, but they are not bit for

@@ -387,12 +387,16 @@ def test_proj_workspace_checks():
 
 
 def test_two_workgroup_rule():
-    """The two-workgroup form: 33-128 pairs that fit twice on the device and
-    at most 2^17 (token, head) pairs, after the decode and segment rules;
-    kernel 6 forces it wherever it fits; a value-split override keeps the
-    single-workgroup kernel."""
+    """The two-workgroup form: 33-96 pairs, or 97-128 pairs and at most 2^17
+    (token, head) pairs, that fit twice on the device, after the decode and
+    segment rules; kernel 6 forces it wherever it fits; a value-split
+    override keeps the single-workgroup kernel."""
     f = kda.kda_debug_two_workgroups
     assert not f(16384, 16, 8)               # 128 pairs x 2048 tokens: 2^18 token-heads
+    assert not f(14336, 16, 7)               # 112 pairs x 2048
+    assert f(12288, 16, 6)                   # 96 pairs x 2048: any length up to 96 pairs
+    assert f(32768, 8, 8)                    # 64 pairs x 4096
+    assert f(16384, 8, 16)                   # 128 pairs x 1024: 2^17 token-heads
     assert f(8192, 16, 4)                    # 64 pairs x 2048
     assert f(16384, 4, 32)                   # 128 pairs x 512
     assert not f(8192, 16, 2)                # 32 pairs (the segment schedule takes it)
