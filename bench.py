@@ -188,6 +188,9 @@ def workload_name(args, dims=None):
         sel += f" --lower-bound {args.lower_bound:g}"
     if args.segments != "auto":
         sel += f" --segments {args.segments}"
+    if getattr(args, "kernel", 0):
+        wl += f"_kernel{args.kernel}"
+        sel += f" --kernel {args.kernel}"
     if args.vsplit:
         sel += f" --vsplit {args.vsplit}"
     if dims is not None:
@@ -205,12 +208,13 @@ def workload_name(args, dims=None):
 
 
 def apply_hooks(args):
-    """The library's test hooks the run asks for: the segment schedule and
-    the value split."""
+    """The library's test hooks the run asks for: the segment schedule, the
+    value split and the kernel family."""
     import gated_delta_rule_tok_amd as kda
     seg = {"auto": 0, "off": 1}.get(args.segments)
     kda.kda_debug_set_segment(int(args.segments) if seg is None else seg)
     kda.kda_debug_set_vsplit(args.vsplit)
+    kda.kda_debug_set_kernel(getattr(args, "kernel", 0))
 
 
 PROJ_K, PROJ_NAB, PROJ_NB = 7168, 144, 1536
@@ -385,6 +389,9 @@ def main():
                          "(sequence, head) pairs: auto, off, or a segment length (multiple of 16)")
     ap.add_argument("--vsplit", type=int, default=0,
                     help="force the value split (1, 2, 4, 8); 0: the library's choice")
+    ap.add_argument("--kernel", type=int, default=0,
+                    help="force a kernel family (kda_debug_set_kernel: 4 the 16-token kernel, 6 its "
+                         "two-workgroup form, ...); 0: the library's choice.  Not the headline number")
     ap.add_argument("--proj", type=int, default=0, metavar="M",
                     help="instead of the forward: time the gate / beta projections (kda_gate_proj) "
                          "for M tokens at hidden 7168, 144 = 128 + 16 rows, 1536 gate columns")

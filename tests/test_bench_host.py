@@ -94,4 +94,6 @@ def test_bench_labels_the_two_workgroup_workloads():
     assert bench.workload_name(a)[1] == "pipe_kernel"
     a.uniform, a.vsplit = "32,512,4", 2
     assert bench.workload_name(a)[1] == "pipe_kernel"
-    bench.apply_hooks(argparse.Namespace(segments="auto", vsplit=0))
+    a.uniform, a.vsplit, a.kernel = None, 0, 6     # forced: the headline shape in two workgroups
+    assert bench.workload_name(a) == ("varlen_8x2048_h16_kernel6", "duo_kernel", "--config 1 --kernel 6")
+    bench.apply_hooks(argparse.Namespace(segments="auto", vsplit=0, kernel=0))
