@@ -22,9 +22,12 @@
 // Producer workgroup: ten producer waves build the packages of five chunk
 // slots in LDS, two waves a chunk (the 64-channel halves, as in the
 // single-workgroup kernel); two copy waves (even and odd chunks) copy each
-// finished package into the item's ring in the workspace, slot chunk mod
-// kDuoRing, once the consumer has taken the package that last held it, wait
-// for their stores, and publish the count of their chunks in a flag word.
+// finished package into the item's ring of kDuoRing (4) packages in the
+// workspace, slot chunk mod kDuoRing, once the consumer has taken the package
+// that last held it, wait for their stores, and publish the count of their
+// chunks in a flag word.  A short ring keeps each slot's reuse within what
+// the XCD's L2 holds: with 8 slots most packages were written back to HBM
+// before they were read.
 //
 // Consumer workgroup: eight state waves (one 16-column strip each) and two
 // loader waves (even and odd chunks, matching the copy waves).  A loader
@@ -39,9 +42,9 @@
 //
 // Flags: one uint64 word per writer, (nonce << 32) | (xcc << 28) | count.
 // The nonce is a per-call value from the host, so words left by an earlier
-// call (or other data of the workspace) are never taken for this call's; the
-// consumer clears the item's words when it is done, so a graph replayed with
-// the same nonce starts from zero again.  xcc is the XCD of the publishing
+// call (or other data of the workspace) are never taken for this call's; each
+// loader clears its parity's two words when it is done, so a graph replayed
+// with the same nonce starts from zero again.  xcc is the XCD of the publishing
 // workgroup: the loader checks it against its own (a pair split over two XCDs
 // would not see each other's stores in one L2) and reports a mismatch in the
 // status word (2).  Polls read the words with scalar loads that bypass the
