@@ -282,3 +282,19 @@ def test_duo_strided_views():
     assert bool((obuf[..., :128].view(torch.int16) == SENTINEL).all()), "wrote outside out"
     oref, fref = run_oracle(x)
     assert_parity(x, out_s, fin_s, oref, fref, label="two workgroups, strided views")
+
+
+def test_duo_full_size_against_oracle():
+    """4 x 2048 tokens, 16 heads (64 pairs, the automatic choice), fp32 initial
+    state: every output and final-state element against the oracle."""
+    import torch
+    x = KI.make_inputs([2048] * 4, 16, seed=99, init_state="fp32")
+    print(f"[case] duo 4x2048 h16 against the oracle", flush=True)
+    d = to_device(x)
+    out, fin, _ = alloc_outputs(x, d)
+    ws = _patterned_workspace(x)
+    run_gpu(x, d, out=out, fin=fin, ws=ws)
+    torch.cuda.synchronize()
+    assert _ran_duo(ws, x)
+    oref, fref = run_oracle(x)
+    assert_parity(x, out, fin, oref, fref, label="two workgroups, 4x2048 h16")
