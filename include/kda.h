@@ -410,7 +410,11 @@ int32_t kda_debug_segment_length(int64_t num_tokens, int32_t heads, int32_t num_
  * producer and a consumer of all 128 value columns, bit for bit the same
  * results) for 33 to 96 (sequence, head) pairs, and for 97 to 128 pairs in
  * calls of at most 2^17 (token, head) pairs, when twice the pair count fits
- * on the device's compute units and the workspace holds its second part.  The
+ * on the device's compute units and the workspace holds its second part.
+ * The two workgroups of a pair hand the chunks over while both run, so that
+ * form needs the compute units the call's grid asks for: on a device whose
+ * other compute units are held by kernels that never end, its bounded waits
+ * give up (status word 1) instead of completing.  The
  * choice is by the batch's average, so one sequence's result may come from
  * either kernel depending on what it is batched with: both follow the
  * recurrence within the tolerances of the oracle, but they are not bit for
