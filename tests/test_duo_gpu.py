@@ -298,3 +298,35 @@ def test_duo_full_size_against_oracle():
     assert _ran_duo(ws, x)
     oref, fref = run_oracle(x)
     assert_parity(x, out, fin, oref, fref, label="two workgroups, 4x2048 h16")
+
+
+def test_paths_without_the_form_give_its_bits():
+    """40 pairs (5 sequences x 8 heads): the plain forward takes the
+    two-workgroup form; the checkpoint entry point (interval 256) and the
+    no-allocation entry point never do, and give the same out and final
+    state bit for bit."""
+    import torch
+    import gated_delta_rule_tok_amd as kda
+    x = KI.make_inputs([1000, 700, 512, 1300, 256], 8, seed=100, init_state="fp32")
+    print(f"[case] duo vs checkpoint and no-allocation paths", flush=True)
+    d = to_device(x)
+    out, fin, _ = alloc_outputs(x, d)
+    ws = _patterned_workspace(x)
+    run_gpu(x, d, out=out, fin=fin, ws=ws)
+    torch.cuda.synchronize()
+    assert _ran_duo(ws, x)
+    ck = torch.empty(x.T // 256, x.H, D, D, dtype=torch.float32, device="cuda")  # the capacity asked for
+    out_c, fin_c, ws_c = alloc_outputs(x, d)
+    kda.kda_chunk_prefill_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"],
+                              x.lower_bound, x.scale, d["s0"], d["cu"], out_c, fin_c, ws_c,
+                              checkpoints=ck, checkpoint_interval=256)
+    out_n, fin_n, _ = alloc_outputs(x, d)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kda.kda_chunk_prefill_fwd_noalloc(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"],
+                                      d["dt_bias"], x.lower_bound, x.scale, d["s0"], d["cu"],
+                                      out_n, fin_n, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for o, f, what in ((out_c, fin_c, "checkpoint call"), (out_n, fin_n, "no-allocation call")):
+        _same_bits(o, out, f"{what} out")
+        _same_bits(f, fin, f"{what} final state")
